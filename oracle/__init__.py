@@ -1,0 +1,228 @@
+"""fp64 CPU oracle for GQA attention forward and split-K paged decode.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the CPU-baseline leg
+of the benchmark may import this package; the HIP library and its Python
+binding never do, and this package never imports them.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, OpenMP over query rows);
+this module only marshals torch CPU tensors into it and returns numpy float64
+arrays.  Which passages of the pages each function follows is stated in the C
+source next to each function.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# The mutation tests point this at a deliberately broken build of oracle.c.
+_LIB_OVERRIDE = os.environ.get("GQA_ORACLE_LIB")
+
+_DT = {torch.float64: 0, torch.float32: 1, torch.float16: 2, torch.bfloat16: 3}
+
+_lib = None
+
+
+def build(src: str = _SRC, out: str = LIB_PATH) -> str:
+    """Compile oracle.c (or a given copy of it) into a shared library with gcc."""
+    tmp = out + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall",
+           "-Wextra", "-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if _LIB_OVERRIDE:
+        lib = ctypes.CDLL(_LIB_OVERRIDE)
+    else:
+        if not os.path.exists(LIB_PATH):
+            build()
+        lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+    lib.oracle_widen.argtypes = [vp, i32, i64, vp]
+    lib.oracle_widen.restype = None
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = i32
+    lib.oracle_attn_fwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                    f64, i32, vp, i64, vp, vp]
+    lib.oracle_attn_fwd.restype = i32
+    lib.oracle_softmax_matrix.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                          f64, i32, i32, i32, vp]
+    lib.oracle_softmax_matrix.restype = i32
+    lib.oracle_attn_decode.argtypes = [vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
+                                       i32, i32, f64, vp, i64, vp, vp]
+    lib.oracle_attn_decode.restype = i32
+    lib.oracle_decode_split_merge.argtypes = [vp, vp, vp, i32, vp, vp, i32, i32, i32, i32,
+                                              i32, i32, i32, f64, vp, i32, vp, i64, vp, vp,
+                                              vp, vp]
+    lib.oracle_decode_split_merge.restype = i32
+    _lib = lib
+    return lib
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle runs on."""
+    return int(_load().oracle_num_threads())
+
+
+def _cpu(t: torch.Tensor, dtype=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        t = torch.as_tensor(t)
+    t = t.detach().to("cpu")
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.contiguous()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _np_ptr(a):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def _dt(*ts):
+    dts = {t.dtype for t in ts}
+    if len(dts) != 1:
+        raise TypeError(f"q/k/v must share one dtype, got {dts}")
+    dt = dts.pop()
+    if dt not in _DT:
+        raise TypeError(f"unsupported dtype {dt}")
+    return _DT[dt]
+
+
+def _rows(rows):
+    if rows is None:
+        return None
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    return r
+
+
+def widen(t: torch.Tensor) -> np.ndarray:
+    """The oracle's own storage-format -> float64 conversion (for pinning it)."""
+    t = _cpu(t)
+    out = np.empty(t.numel(), dtype=np.float64)
+    _load().oracle_widen(_ptr(t), _DT[t.dtype], t.numel(), _np_ptr(out))
+    return out.reshape(tuple(t.shape))
+
+
+def attn_fwd(q, k, v, scale: float, causal: bool, rows=None):
+    """Plain attention forward.
+
+    q [B, Hq, q_len, D], k/v [B, Hkv, kv_len, D] (one storage dtype).
+    Returns (o, lse): with rows=None, o [B, Hq, q_len, D] and lse [B, Hq, q_len];
+    otherwise o [n, D] and lse [n] for the flat row ids (b*Hq + h)*q_len + i.
+    `scale` is used exactly as given (pass the fp32 value the GPU receives).
+    """
+    q, k, v = _cpu(q), _cpu(k), _cpu(v)
+    dt = _dt(q, k, v)
+    B, Hq, q_len, D = q.shape
+    _, Hkv, kv_len, _ = k.shape
+    r = _rows(rows)
+    n = B * Hq * q_len if r is None else r.shape[0]
+    o = np.empty((n, D), dtype=np.float64)
+    lse = np.empty((n,), dtype=np.float64)
+    rc = _load().oracle_attn_fwd(_ptr(q), _ptr(k), _ptr(v), dt, B, Hq, Hkv, q_len, kv_len, D,
+                                 float(scale), int(bool(causal)), _np_ptr(r), n,
+                                 _np_ptr(o), _np_ptr(lse))
+    if rc:
+        raise ValueError("oracle_attn_fwd: bad arguments")
+    if r is None:
+        return o.reshape(B, Hq, q_len, D), lse.reshape(B, Hq, q_len)
+    return o, lse
+
+
+def softmax_matrix(q, k, scale: float, causal: bool, b: int, h: int) -> np.ndarray:
+    """Materialised softmax P [q_len, kv_len] of one (b, h)."""
+    q, k = _cpu(q), _cpu(k)
+    dt = _dt(q, k)
+    B, Hq, q_len, D = q.shape
+    _, Hkv, kv_len, _ = k.shape
+    p = np.empty((q_len, kv_len), dtype=np.float64)
+    rc = _load().oracle_softmax_matrix(_ptr(q), _ptr(k), dt, B, Hq, Hkv, q_len, kv_len, D,
+                                       float(scale), int(bool(causal)), b, h, _np_ptr(p))
+    if rc:
+        raise ValueError("oracle_softmax_matrix: bad arguments")
+    return p
+
+
+def _decode_common(q, k, v, seq_lens, block_table, max_kv_len):
+    q, k, v = _cpu(q), _cpu(k), _cpu(v)
+    dt = _dt(q, k, v)
+    B, Hq, D = q.shape
+    sl = _cpu(seq_lens, torch.int32)
+    if block_table is not None:
+        bt = _cpu(block_table, torch.int32)
+        max_pages = bt.shape[1]
+        page_size = k.shape[1]
+        Hkv = k.shape[2]
+        if max_kv_len is None:
+            max_kv_len = max_pages * page_size
+    else:
+        bt = None
+        max_pages, page_size = 0, 0
+        Hkv = k.shape[1]
+        if max_kv_len is None:
+            max_kv_len = k.shape[2]
+    return q, k, v, dt, B, Hq, D, sl, bt, max_pages, page_size, Hkv, int(max_kv_len)
+
+
+def attn_decode(q, k, v, seq_lens, scale: float, block_table=None, max_kv_len=None, rows=None):
+    """Decode (q_len = 1) over a paged pool (block_table given) or dense [B, Hkv, L, D] K/V.
+
+    Returns (o [B, Hq, D], lse [B, Hq]) or, with rows, (o [n, D], lse [n]) for
+    flat ids b*Hq + h.
+    """
+    q, k, v, dt, B, Hq, D, sl, bt, max_pages, page_size, Hkv, max_kv_len = _decode_common(
+        q, k, v, seq_lens, block_table, max_kv_len)
+    r = _rows(rows)
+    n = B * Hq if r is None else r.shape[0]
+    o = np.empty((n, D), dtype=np.float64)
+    lse = np.empty((n,), dtype=np.float64)
+    rc = _load().oracle_attn_decode(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(sl), _ptr(bt), max_pages,
+                                    page_size, B, Hq, Hkv, D, max_kv_len, float(scale),
+                                    _np_ptr(r), n, _np_ptr(o), _np_ptr(lse))
+    if rc:
+        raise ValueError("oracle_attn_decode: bad arguments")
+    if r is None:
+        return o.reshape(B, Hq, D), lse.reshape(B, Hq)
+    return o, lse
+
+
+def decode_split_merge(q, k, v, seq_lens, scale: float, bounds, block_table=None,
+                       max_kv_len=None, rows=None):
+    """Decode computed chunk by chunk and merged through the chunks' LSEs.
+
+    bounds: int array [B, n_splits + 1] of chunk edges per sequence.
+    Returns (o, lse, o_parts, lse_parts) with o [n, D], lse [n],
+    o_parts [n, n_splits, D], lse_parts [n, n_splits] over flat ids b*Hq + h.
+    """
+    q, k, v, dt, B, Hq, D, sl, bt, max_pages, page_size, Hkv, max_kv_len = _decode_common(
+        q, k, v, seq_lens, block_table, max_kv_len)
+    bnd = _cpu(torch.as_tensor(bounds), torch.int32)
+    n_splits = bnd.shape[1] - 1
+    r = _rows(rows)
+    n = B * Hq if r is None else r.shape[0]
+    o = np.empty((n, D), dtype=np.float64)
+    lse = np.empty((n,), dtype=np.float64)
+    op = np.empty((n, n_splits, D), dtype=np.float64)
+    lp = np.empty((n, n_splits), dtype=np.float64)
+    rc = _load().oracle_decode_split_merge(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(sl), _ptr(bt),
+                                           max_pages, page_size, B, Hq, Hkv, D, max_kv_len,
+                                           float(scale), _ptr(bnd), n_splits, _np_ptr(r), n,
+                                           _np_ptr(o), _np_ptr(lse), _np_ptr(op), _np_ptr(lp))
+    if rc:
+        raise ValueError("oracle_decode_split_merge: bad arguments")
+    return o, lse, op, lp

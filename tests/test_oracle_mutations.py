@@ -1,0 +1,55 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each case copies oracle.c, applies one plausible mistake (a dropped term, a
+wrong sign, index or base, a wrong head map, a shifted mask), builds the copy
+with gcc and runs the pin suite against it in a child process.  The pins pass
+on the real oracle (test_oracle.py); here at least one of them must fail for
+every mutant.  Everything runs on the CPU.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+MUTANTS = {
+    "head_map_modulo": ("int g = h / group;\n            kv_view kv = {k, v, dt, D, ((int64_t)b * Hkv + g) * kv_len",
+                        "int g = h % Hkv;\n            kv_view kv = {k, v, dt, D, ((int64_t)b * Hkv + g) * kv_len"),
+    "causal_off_by_one": ("int64_t vis_end = causal ? i + 1 + delta : (int64_t)kv_len;\n            attend_one(q, r",
+                          "int64_t vis_end = causal ? i + delta : (int64_t)kv_len;\n            attend_one(q, r"),
+    "causal_top_left": ("int64_t vis_end = causal ? i + 1 + delta : (int64_t)kv_len;\n            attend_one(q, r",
+                        "int64_t vis_end = causal ? i + 1 : (int64_t)kv_len;\n            attend_one(q, r"),
+    "lse_base_two": ("double L = m + log(z);", "double L = m + log2(z);"),
+    "scale_dropped": ("s[t - lo] = scale * acc;", "s[t - lo] = acc;"),
+    "max_not_subtracted": ("z += exp(s[t - lo] - m);", "z += exp(s[t - lo]);"),
+    "prob_sign_flipped": ("double p = exp(s[t - lo] - L);", "double p = exp(L - s[t - lo]);"),
+    "values_read_from_keys": ("o[d] += p * elem(kv->v,", "o[d] += p * elem(kv->k,"),
+    "value_feature_shifted": ("o[d] += p * elem(kv->v, kv_index(kv, t, d), kv->dt);",
+                              "o[d] += p * elem(kv->v, kv_index(kv, t, (d + 1) % D), kv->dt);"),
+    "empty_row_lse_zero": ("*lse = -INFINITY;\n        return;", "*lse = 0.0;\n        return;"),
+    "page_row_shifted": ("int64_t row = t % kv->page_size;", "int64_t row = (t + 1) % kv->page_size;"),
+    "merge_weight_sign": ("double w = exp(ls[sp] - M);", "double w = exp(M - ls[sp]);"),
+    "merge_lse_dropped_max": ("lse_out[n] = M + log(wsum);", "lse_out[n] = log(wsum);"),
+    "half_exponent_bias": ("v = ldexp((double)(m | 0x400), e - 25);", "v = ldexp((double)(m | 0x400), e - 24);"),
+    "bf16_shift": ("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique/present"
+    mutated = tmp_path / "oracle_mutant.c"
+    mutated.write_text(src.replace(old, new))
+    sys.path.insert(0, ROOT)
+    import oracle
+    lib = oracle.build(str(mutated), str(tmp_path / "liboracle_mutant.so"))
+    env = dict(os.environ, GQA_ORACLE_LIB=lib, OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutant {name} survived the oracle pins:\n{r.stdout[-2000:]}"

@@ -1,0 +1,143 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
+
+This module only draws random numbers and lays them out: it holds none of the
+attention arithmetic, and it imports neither the HIP binding nor the oracle.
+Every tensor is drawn on the CPU from ``torch.Generator().manual_seed(seed)``,
+in fp32 from N(0, 1), optionally multiplied by an exact power of two, and then
+rounded (round-to-nearest-even) to the storage dtype.  The rounded host copy
+is what both the GPU and the oracle consume.
+
+Workloads (shapes of the attention problems the pages state):
+  causal_gqa_fp32       B=1 Hq=4 Hkv=2 S=128 D=64, fp32, causal
+  causal_gqa_prefill    B=2 Hq=32 Hkv=8 S=2048 D=128, bf16, causal
+  causal_gqa_offset     B=1 Hq=32 Hkv=4 q_len=1024 kv_len=4096 D=128, bf16,
+                        causal with the bottom-right offset (delta = 3072)
+  mha_noncausal_fp16    B=4 H=16 S=4096 D=64, fp16, inputs x0.5, non-causal
+  paged_decode          B=16 Hq=32 Hkv=8 D=128, bf16, kv_len ~ U[1024, 32768],
+                        256-token pages placed by a seeded permutation, 16 splits
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def fp32_scale(D: int) -> float:
+    """1/sqrt(D) rounded to fp32: the exact scale value both sides receive."""
+    return float(np.float32(1.0 / math.sqrt(D)))
+
+
+@dataclass(frozen=True)
+class PrefillSpec:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    q_len: int
+    kv_len: int
+    D: int
+    dtype: str
+    causal: bool
+    seed: int
+    mult: float = 1.0
+
+
+@dataclass(frozen=True)
+class DecodeSpec:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    dtype: str
+    len_lo: int
+    len_hi: int          # inclusive
+    page_size: int
+    max_pages: int
+    n_splits: int
+    seed: int
+
+
+CAUSAL_GQA_FP32 = PrefillSpec("causal_gqa_fp32", 1, 4, 2, 128, 128, 64, "f32", True, 20261)
+CAUSAL_GQA_PREFILL = PrefillSpec("causal_gqa_prefill", 2, 32, 8, 2048, 2048, 128, "bf16", True, 20262)
+CAUSAL_GQA_OFFSET = PrefillSpec("causal_gqa_offset", 1, 32, 4, 1024, 4096, 128, "bf16", True, 20263)
+MHA_NONCAUSAL_FP16 = PrefillSpec("mha_noncausal_fp16", 4, 16, 16, 4096, 4096, 64, "f16", False, 20264, 0.5)
+PAGED_DECODE = DecodeSpec("paged_decode", 16, 32, 8, 128, "bf16", 1024, 32768, 256, 128, 16, 20265)
+
+PREFILL_WORKLOADS = [CAUSAL_GQA_FP32, CAUSAL_GQA_PREFILL, CAUSAL_GQA_OFFSET, MHA_NONCAUSAL_FP16]
+
+
+def _randn(shape, g, dtype, mult=1.0):
+    x = torch.randn(shape, dtype=torch.float32, generator=g)
+    if mult != 1.0:
+        x.mul_(mult)  # the multipliers used are powers of two: exact in fp32
+    return x.to(dtype)
+
+
+def make_prefill(B, Hq, Hkv, q_len, kv_len, D, dtype="bf16", seed=0, mult=1.0):
+    """Q [B,Hq,q_len,D], K/V [B,Hkv,kv_len,D] on the CPU, drawn in the order Q, K, V."""
+    g = torch.Generator().manual_seed(seed)
+    dt = _DTYPES[dtype]
+    q = _randn((B, Hq, q_len, D), g, dt, mult)
+    k = _randn((B, Hkv, kv_len, D), g, dt, mult)
+    v = _randn((B, Hkv, kv_len, D), g, dt, mult)
+    return q, k, v
+
+
+def make_prefill_spec(spec: PrefillSpec):
+    return make_prefill(spec.B, spec.Hq, spec.Hkv, spec.q_len, spec.kv_len, spec.D,
+                        spec.dtype, spec.seed, spec.mult)
+
+
+@dataclass
+class DecodeInputs:
+    q: torch.Tensor            # [B, Hq, D]
+    k_cache: torch.Tensor      # [num_pages, page_size, Hkv, D]
+    v_cache: torch.Tensor
+    seq_lens: torch.Tensor     # [B] int32
+    block_table: torch.Tensor  # [B, max_pages] int32, -1 padding
+    page_size: int
+    max_kv_len: int
+
+
+def make_decode(B, Hq, Hkv, D, dtype="bf16", seed=0, len_lo=1, len_hi=64, page_size=256,
+                max_pages: Optional[int] = None, seq_lens=None, permute=True):
+    """Paged decode inputs, drawn in the order q, seq_lens, page permutation, K, V.
+
+    Sequence b uses n_b = ceil(len_b / page_size) pages; pages are handed out
+    from a seeded permutation of all pages (identity when permute=False) in
+    sequence order; unused block-table slots hold -1.
+    """
+    g = torch.Generator().manual_seed(seed)
+    dt = _DTYPES[dtype]
+    q = _randn((B, Hq, D), g, dt)
+    if seq_lens is None:
+        seq_lens = torch.randint(len_lo, len_hi + 1, (B,), generator=g, dtype=torch.int64)
+    seq_lens = torch.as_tensor(seq_lens, dtype=torch.int64)
+    n_pages = [(int(s) + page_size - 1) // page_size for s in seq_lens]
+    total_pages = max(1, sum(n_pages))
+    perm = torch.randperm(total_pages, generator=g) if permute else torch.arange(total_pages)
+    if max_pages is None:
+        max_pages = max(1, max(n_pages) if n_pages else 1)
+    bt = torch.full((B, max_pages), -1, dtype=torch.int32)
+    off = 0
+    for b, n in enumerate(n_pages):
+        if n > max_pages:
+            raise ValueError("sequence needs more pages than max_pages")
+        bt[b, :n] = perm[off:off + n].to(torch.int32)
+        off += n
+    k = _randn((total_pages, page_size, Hkv, D), g, dt)
+    v = _randn((total_pages, page_size, Hkv, D), g, dt)
+    return DecodeInputs(q, k, v, seq_lens.to(torch.int32), bt, page_size, max_pages * page_size)
+
+
+def make_decode_spec(spec: DecodeSpec):
+    return make_decode(spec.B, spec.Hq, spec.Hkv, spec.D, spec.dtype, spec.seed,
+                       spec.len_lo, spec.len_hi, spec.page_size, spec.max_pages)
+
