@@ -1,0 +1,151 @@
+"""Python binding of libgqa_attn.so (the C ABI in include/gqa_attn.h).
+
+Argument marshalling only: torch supplies device memory and the current HIP
+stream; every step of the computation runs in the library's HIP kernels.
+There is no fallback path: if the library is not built, or a call returns an
+error status, these functions raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgqa_attn.so")
+
+GQA_F32, GQA_F16, GQA_BF16 = 0, 1, 2
+STATUS = {0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_UNSUPPORTED",
+          3: "GQA_ERR_WORKSPACE", 4: "GQA_ERR_HIP"}
+_TORCH_DT = {torch.float32: GQA_F32, torch.float16: GQA_F16, torch.bfloat16: GQA_BF16}
+
+# Every symbol include/gqa_attn.h declares.
+EXPORTS = ("attn_fwd", "attn_decode_workspace_bytes", "attn_decode_splitk", "attn_status_str")
+
+_lib = None
+
+
+class GqaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library with argument types declared (raises if not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                           "python -m gqa_attention_forward_attn_amd.build")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32, vp]
+    L.attn_fwd.restype = i32
+    L.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    L.attn_decode_workspace_bytes.restype = sz
+    L.attn_decode_splitk.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                     f32, i32, vp, sz, i32, vp]
+    L.attn_decode_splitk.restype = i32
+    L.attn_status_str.argtypes = [i32]
+    L.attn_status_str.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        raise GqaError(fn, rc)
+
+
+def default_scale(D: int) -> float:
+    return 1.0 / math.sqrt(D)
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
+             scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+             lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Attention forward. q [B,Hq,q_len,D], k/v [B,Hkv,kv_len,D] on one GPU.
+
+    Returns (o [B,Hq,q_len,D] in q's dtype, lse [B,Hq,q_len] fp32, natural log).
+    Causal masking is bottom-right aligned (query i sees keys j <= i + kv_len - q_len).
+    """
+    B, Hq, q_len, D = q.shape
+    Bk, Hkv, kv_len, Dk = k.shape
+    if Bk != B or Dk != D or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("shape mismatch between q, k and v")
+    if q.dtype not in _TORCH_DT or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype among float32/float16/bfloat16")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("inputs must be contiguous GPU tensors")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, q_len), dtype=torch.float32, device=q.device)
+    sc = default_scale(D) if scale is None else float(scale)
+    rc = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, q_len, kv_len, D,
+                        sc, int(bool(causal)), _TORCH_DT[q.dtype], _stream(q.device))
+    _check("attn_fwd", rc)
+    return out, lse
+
+
+def decode_workspace_bytes(B: int, Hq: int, D: int, n_splits: int) -> int:
+    return int(lib().attn_decode_workspace_bytes(B, Hq, D, n_splits))
+
+
+def attn_decode_splitk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens: torch.Tensor,
+                       block_table: Optional[torch.Tensor] = None, n_splits: int = 16,
+                       scale: Optional[float] = None, max_kv_len: Optional[int] = None,
+                       workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                       lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Split-K decode. q [B,Hq,D]; paged k/v [pages,page_size,Hkv,D] with block_table
+    [B,max_pages] int32, or dense k/v [B,Hkv,max_kv_len,D] with block_table None.
+
+    Returns (o [B,Hq,D], lse [B,Hq] fp32).  `workspace` (uint8, >= decode_workspace_bytes)
+    may be passed to avoid an allocation per call.
+    """
+    B, Hq, D = q.shape
+    if block_table is not None:
+        _, page_size, Hkv, _ = k.shape
+        max_pages = block_table.shape[1]
+        if max_kv_len is None:
+            max_kv_len = max_pages * page_size
+        if block_table.dtype != torch.int32 or not block_table.is_contiguous():
+            raise TypeError("block_table must be a contiguous int32 tensor")
+    else:
+        _, Hkv, L, _ = k.shape
+        page_size, max_pages = 0, 0
+        if max_kv_len is None:
+            max_kv_len = L
+    if seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous():
+        raise TypeError("seq_lens must be a contiguous int32 tensor")
+    if q.dtype not in _TORCH_DT or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    need = decode_workspace_bytes(B, Hq, D, n_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    sc = default_scale(D) if scale is None else float(scale)
+    rc = lib().attn_decode_splitk(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(seq_lens),
+                                  _ptr(block_table), max_pages, page_size, B, Hq, Hkv, D,
+                                  int(max_kv_len), sc, int(n_splits), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(),
+                                  _TORCH_DT[q.dtype], _stream(q.device))
+    _check("attn_decode_splitk", rc)
+    return out, lse

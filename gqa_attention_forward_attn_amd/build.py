@@ -1,0 +1,71 @@
+"""Build libgqa_attn.so in-tree: hipcc for gfx950, one object per source, then link.
+
+Run as a script (``python -m gqa_attention_forward_attn_amd.build``) or call
+``build()``.  Every source is compiled each time it is called.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+OBJ_DIR = os.path.join(PKG, "_build")
+LIB_PATH = os.path.join(PKG, "libgqa_attn.so")
+SOURCES = ["prefill_fwd.hip", "decode_splitk.hip", "api.cpp"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
+
+
+def compile_flags(save_temps: bool = False) -> list:
+    flags = [
+        "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+        "-I" + INCLUDE, "-I" + CSRC,
+        # packed fp32 VALU forms stay off: plain fp32 code only
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wall", "-Wno-unused-function",
+    ]
+    if save_temps:
+        flags.append("-save-temps=obj")
+    return flags
+
+
+def _compile(src: str, save_temps: bool) -> str:
+    obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc()] + compile_flags(save_temps) + ["-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True, cwd=OBJ_DIR)
+    # the host pass does not know the gfx950 feature name; that warning is expected
+    noise = "is not a recognized feature for this target"
+    msg = "\n".join(line for line in (r.stdout + r.stderr).splitlines() if noise not in line)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{msg}")
+    if msg.strip():
+        print(msg, file=sys.stderr)
+    return obj
+
+
+def build(save_temps: bool = False) -> str:
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, save_temps), SOURCES))
+    tmp = LIB_PATH + ".tmp"
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(save_temps="--save-temps" in sys.argv))

@@ -1,0 +1,123 @@
+// api.cpp - the extern "C" boundary declared in include/gqa_attn.h: argument
+// validation (before any HIP call), instantiation choice and launch on the
+// caller's stream.  No allocation, no synchronisation, no global state.
+#include "gqa_attn.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+#include "gqa_kernels.hpp"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+bool supported_head_dim(int D) { return D == 64 || D == 128; }
+
+bool valid_dtype(gqa_dtype_t t) { return t == GQA_F32 || t == GQA_F16 || t == GQA_BF16; }
+
+int to_kernel_dtype(gqa_dtype_t t) {
+    switch (t) {
+    case GQA_F16: return gqa::kDtypeF16;
+    case GQA_BF16: return gqa::kDtypeBF16;
+    default: return gqa::kDtypeF32;
+    }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+gqa_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int Hq, int Hkv, int q_len, int kv_len, int D,
+                      float scale, int causal, gqa_dtype_t dtype, void* hip_stream) {
+    if (B < 0 || q_len < 0 || kv_len < 0 || Hq <= 0 || Hkv <= 0 || D <= 0) return GQA_ERR_INVALID_ARG;
+    if (Hq % Hkv != 0) return GQA_ERR_INVALID_ARG;
+    if (!valid_dtype(dtype)) return GQA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return GQA_ERR_INVALID_ARG;
+    if (!supported_head_dim(D)) return GQA_ERR_UNSUPPORTED;
+    if (B == 0 || q_len == 0) return GQA_OK;
+    if (!q || !o || !lse) return GQA_ERR_INVALID_ARG;
+    if (kv_len > 0 && (!k || !v)) return GQA_ERR_INVALID_ARG;
+    // 16-byte vector loads/stores need 16-byte aligned tensors
+    if (!aligned16(q) || !aligned16(o) || (kv_len > 0 && (!aligned16(k) || !aligned16(v))))
+        return GQA_ERR_INVALID_ARG;
+    // rows and elements must fit the kernels' index arithmetic
+    const long long rows_q = (long long)B * Hq * q_len;
+    const long long rows_kv = (long long)B * Hkv * kv_len;
+    if (rows_q > (1LL << 40) || rows_kv > (1LL << 40)) return GQA_ERR_INVALID_ARG;
+
+    gqa::PrefillArgs a{};
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.q_len = q_len; a.kv_len = kv_len;
+    a.group = Hq / Hkv;
+    a.delta = kv_len - q_len;
+    a.c = scale * kLog2e;
+    hipError_t e = gqa::launch_prefill(a, D, causal != 0, to_kernel_dtype(dtype),
+                                       static_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+size_t attn_decode_workspace_bytes(int B, int Hq, int D, int n_splits) {
+    if (B <= 0 || Hq <= 0 || D <= 0 || n_splits <= 0) return 0;
+    return (size_t)B * (size_t)Hq * (size_t)n_splits * ((size_t)D + 1) * sizeof(float);
+}
+
+gqa_status_t attn_decode_splitk(const void* q, const void* k, const void* v, void* o, float* lse,
+                                const int* seq_lens, const int* block_table,
+                                int max_pages_per_seq, int page_size,
+                                int B, int Hq, int Hkv, int D, int max_kv_len,
+                                float scale, int n_splits,
+                                void* workspace, size_t workspace_bytes,
+                                gqa_dtype_t dtype, void* hip_stream) {
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || max_kv_len < 0) return GQA_ERR_INVALID_ARG;
+    if (Hq % Hkv != 0) return GQA_ERR_INVALID_ARG;
+    if (n_splits < 1 || n_splits > 256) return GQA_ERR_INVALID_ARG;
+    if (!valid_dtype(dtype)) return GQA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return GQA_ERR_INVALID_ARG;
+    int page_shift = 0;
+    if (block_table) {
+        if (page_size <= 0 || (page_size & (page_size - 1)) != 0 || max_pages_per_seq <= 0)
+            return GQA_ERR_INVALID_ARG;
+        if ((long long)max_pages_per_seq * page_size < (long long)max_kv_len) return GQA_ERR_INVALID_ARG;
+        while ((1 << page_shift) < page_size) ++page_shift;
+    }
+    if (!supported_head_dim(D) || dtype == GQA_F32 || Hq / Hkv > 8) return GQA_ERR_UNSUPPORTED;
+    if (B == 0) return GQA_OK;
+    if (!q || !k || !v || !o || !lse || !seq_lens) return GQA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return GQA_ERR_INVALID_ARG;
+    const size_t need = attn_decode_workspace_bytes(B, Hq, D, n_splits);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return GQA_ERR_WORKSPACE;
+
+    gqa::DecodeArgs a{};
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    a.seq_lens = seq_lens;
+    a.block_table = block_table;
+    a.part_o = static_cast<float*>(workspace);
+    a.part_lse = a.part_o + (size_t)B * Hq * n_splits * D;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.group = Hq / Hkv;
+    a.max_pages = max_pages_per_seq;
+    a.page_shift = page_shift;
+    a.max_kv_len = max_kv_len;
+    a.n_splits = n_splits;
+    a.c = scale * kLog2e;
+    hipError_t e = gqa::launch_decode(a, to_kernel_dtype(dtype), static_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+const char* attn_status_str(gqa_status_t s) {
+    switch (s) {
+    case GQA_OK: return "GQA_OK";
+    case GQA_ERR_INVALID_ARG: return "GQA_ERR_INVALID_ARG: invalid argument";
+    case GQA_ERR_UNSUPPORTED: return "GQA_ERR_UNSUPPORTED: no kernel for this head dim / dtype / group";
+    case GQA_ERR_WORKSPACE: return "GQA_ERR_WORKSPACE: workspace missing or too small";
+    case GQA_ERR_HIP: return "GQA_ERR_HIP: HIP launch error";
+    default: return "unknown gqa_status_t";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,119 @@
+// gqa_device.hpp - device-side building blocks for the gfx950 attention kernels:
+// vector types, MFMA wrappers, cross-lane moves and conversions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Storage tags: the element type in memory and the matching MFMA operand type.
+struct bf16_tag {
+    typedef bf16x8 vec8;
+    typedef bf16x2 vec2;
+};
+struct f16_tag {
+    typedef f16x8 vec8;
+    typedef f16x2 vec2;
+};
+
+// D[32x32] += A[32x16] * B[16x32], fp32 accumulate.  Operand layout: lane l
+// holds row/column (l % 32) and 8 consecutive k-slots starting at 8 * (l / 32).
+// Result layout: lane l holds column (l % 32), rows 8*(r/4) + 4*(l/32) + r%4.
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma_32x32x16(f16x8 a, f16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+// fp32: D[32x32] += A[32x2] * B[2x32]; lane l holds k-slot l / 32.
+__device__ __forceinline__ f32x16 mfma_32x32x2(float a, float b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// 2^x on the transcendental unit (v_exp_f32); exp2(-inf) = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Value of x held by lane (l ^ 32), for every lane l.
+__device__ __forceinline__ float xor32(float x) {
+    uint32_t u = __builtin_bit_cast(uint32_t, x);
+    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    // r[0]: lanes 0-31 keep their value, lanes 32-63 receive lanes 0-31;
+    // r[1]: lanes 0-31 receive lanes 32-63, lanes 32-63 keep theirs.
+    uint32_t lane = __lane_id();
+    return __builtin_bit_cast(float, lane < 32 ? r[1] : r[0]);
+}
+
+// DPP lane moves inside rows of 16 lanes.  quad_perm / row_half_mirror /
+// row_mirror controls; bound_ctrl makes lanes without a source read 0.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+// Lane (l ^ mask) via the LDS crossbar (any mask).
+__device__ __forceinline__ float shfl_xor(float x, int mask) {
+    int lane = __lane_id();
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ mask) << 2,
+                                                                  __builtin_bit_cast(int, x)));
+}
+
+// Two fp32 values -> packed pair in the storage type (round to nearest even).
+__device__ __forceinline__ uint32_t pack2(bf16_tag, float a, float b) {
+    bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint32_t pack2(f16_tag, float a, float b) {
+    f16x2 v = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Packed pair in the storage type -> two fp32 values.
+__device__ __forceinline__ float lo_to_f32(bf16_tag, uint32_t u) { return __builtin_bit_cast(float, u << 16); }
+__device__ __forceinline__ float hi_to_f32(bf16_tag, uint32_t u) { return __builtin_bit_cast(float, u & 0xffff0000u); }
+__device__ __forceinline__ float lo_to_f32(f16_tag, uint32_t u) {
+    return (float)__builtin_bit_cast(f16x2, u)[0];
+}
+__device__ __forceinline__ float hi_to_f32(f16_tag, uint32_t u) {
+    return (float)__builtin_bit_cast(f16x2, u)[1];
+}
+
+// fp32 accumulate of a 2-element dot product in the storage type.
+__device__ __forceinline__ float dot2(bf16_tag, uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+__device__ __forceinline__ float dot2(f16_tag, uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
+}
+
+// Select 16-bit halves of two dwords: lo16(a) | lo16(b) << 16, and hi16(a) | hi16(b) << 16.
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
+    return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
+    return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+__device__ __forceinline__ u32x4 ld_global_16(const void* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+}  // namespace gqa

@@ -1,0 +1,51 @@
+// gqa_kernels.hpp - host-visible launch interface of the HIP kernels (internal
+// to the library; the public ABI is include/gqa_attn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace gqa {
+
+constexpr int kDtypeF32 = 0;
+constexpr int kDtypeF16 = 1;
+constexpr int kDtypeBF16 = 2;
+
+struct PrefillArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    int B, Hq, Hkv, q_len, kv_len;
+    int group;        // Hq / Hkv
+    int delta;        // kv_len - q_len (bottom-right causal offset)
+    int n_pos_tiles;  // filled by the launcher
+    int n_rest;       // filled by the launcher
+    float c;          // scale * log2(e)
+};
+
+// Validated arguments only.  D in {64, 128}; dtype one of kDtype*.
+hipError_t launch_prefill(PrefillArgs a, int D, bool causal, int dtype, hipStream_t stream);
+
+struct DecodeArgs {
+    const void* q;            // [B, Hq, D]
+    const void* k;            // paged [pages, page_size, Hkv, D] or dense [B, Hkv, max_kv_len, D]
+    const void* v;
+    void* o;                  // [B, Hq, D]
+    float* lse;               // [B, Hq]
+    const int* seq_lens;      // [B]
+    const int* block_table;   // [B, max_pages] or nullptr (dense)
+    float* part_o;            // workspace [B, Hq, n_splits, D]
+    float* part_lse;          // workspace [B, Hq, n_splits]
+    int B, Hq, Hkv, D, group;
+    int max_pages;
+    int page_shift;           // log2(page_size) (paged)
+    int max_kv_len;           // dense row stride in tokens
+    int n_splits;
+    float c;                  // scale * log2(e)
+};
+
+hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream);
+
+}  // namespace gqa

@@ -1,0 +1,477 @@
+// prefill_fwd.hip - attention forward (prefill) on gfx950 matrix cores.
+//
+// Method: FlashAttention forward with an online softmax, as in
+// causal_forward_kernel.py (`_flash_attention_forward_gqa_kernel`): for each
+// block of queries, stream K/V tiles, compute S = scale * Q K^T, keep a running
+// row max m and row sum l, rescale the fp32 accumulator by exp2(m_old - m_new),
+// add P V, and finish with O = acc / l and the row log-sum-exp.  Scale is folded
+// with log2(e) so every exponential is a single v_exp_f32 (2^x).  Masking is the
+// bottom-right causal rule of the FlashInfer-style prefill page
+// (gpt-o3 / triton6fd1ef, `_gqa_prefill_kernel`: query i sees keys
+// j <= i + kv_len - q_len); tiles right of the diagonal are never visited and
+// only tiles that cross it (or the end of the keys) pay for the mask, the
+// two-phase split of causal_forward_kernel.py.  Empty rows give O = 0 and
+// LSE = -inf (the zero-fill rule of splitk_kernels.py, `_fwd_kernel_splitK`).
+//
+// gfx950 mapping (bf16/fp16):
+//   * a workgroup is 4 wave64s; each wave owns 32 query rows of one head, and
+//     the workgroup's waves cover NH heads of one K/V group (GQA: the K/V tile
+//     staged in LDS once serves every head of the group in the workgroup);
+//   * the score tile is computed transposed, S^T = K Q^T, with
+//     v_mfma_f32_32x32x16 (keys on M, queries on N), so each lane holds one
+//     query's scores and the row max / row sum are in-lane plus one
+//     lane^32 exchange (v_permlane32_swap);
+//   * the P^T accumulator layout feeds the P.V product directly as the MFMA B
+//     operand; V is stored transposed in LDS with the key order permuted so
+//     that the A operand of each 16-key step is one 16-byte LDS read;
+//   * K/V tiles are double buffered in LDS: the global loads of tile t+1 are in
+//     flight while tile t is multiplied, one barrier per tile.
+#include "gqa_device.hpp"
+#include "gqa_kernels.hpp"
+
+namespace gqa {
+
+namespace {
+
+template <class TAG, int D, bool CAUSAL, int NH>
+__global__ __launch_bounds__(256) void prefill_fwd_mfma(PrefillArgs a) {
+    constexpr int BN = 64;                 // keys per tile
+    constexpr int WPH = 4 / NH;            // waves per head
+    constexpr int POS = 32 * WPH;          // query positions per workgroup
+    constexpr int KS = D + 8;              // K tile row stride (elements)
+    constexpr int VS = BN + 8;             // V^T tile row stride (elements)
+    constexpr int KT = BN * KS;            // elements of one K tile
+    constexpr int VT = D * VS;             // elements of one V^T tile
+    constexpr int DS = D / 16;             // MFMA k-steps over the head dim
+    constexpr int DT = D / 32;             // 32-wide output tiles over the head dim
+    constexpr int KCH = BN * D / 8 / 256;  // 16-byte K chunks per thread per tile
+    constexpr int VTHREADS = 16 * (D / 8); // threads that stage V (4 keys x 8 dims each)
+    typedef typename TAG::vec8 vec8;
+
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (KT + VT)];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int half = lane >> 5;
+    const int l32 = lane & 31;
+
+    // ---- work item: (position tile, batch, K/V head, head group) ----------
+    int pt = blockIdx.x / a.n_rest;
+    int rest = blockIdx.x - pt * a.n_rest;
+    if (CAUSAL) pt = a.n_pos_tiles - 1 - pt;  // longest rows first
+    const int hgroups = a.group / NH;
+    const int hg = rest % hgroups;
+    rest /= hgroups;
+    const int g = rest % a.Hkv;
+    const int b = rest / a.Hkv;
+    const int h = g * a.group + hg * NH + wave / WPH;
+    const int wg_pos0 = pt * POS;
+    const int pos0 = wg_pos0 + (wave % WPH) * 32;
+    const int my_q = pos0 + l32;
+
+    // ---- key ranges -------------------------------------------------------
+    // wg_kv_end: keys any row of the workgroup sees; wave_kv_end: keys any row
+    // of this wave sees; wave_full_end: keys every row of this wave sees.
+    int wg_kv_end = a.kv_len, wave_kv_end = a.kv_len, wave_full_end = a.kv_len;
+    if (CAUSAL) {
+        const int wg_last = min(wg_pos0 + POS, a.q_len) - 1;
+        wg_kv_end = max(0, min(a.kv_len, wg_last + a.delta + 1));
+        const int w_last = min(pos0 + 32, a.q_len) - 1;
+        wave_kv_end = pos0 < a.q_len ? max(0, min(a.kv_len, w_last + a.delta + 1)) : 0;
+        wave_full_end = max(0, min(a.kv_len, pos0 + a.delta + 1));
+    } else if (pos0 >= a.q_len) {
+        wave_kv_end = 0;
+    }
+    const int n_tiles = (wg_kv_end + BN - 1) / BN;
+
+    // ---- Q: B operand of S^T = K Q^T, resident in registers ---------------
+    const size_t q_head = ((size_t)b * a.Hq + h) * (size_t)a.q_len;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + q_head * D;
+    const int q_row = min(my_q, a.q_len - 1);
+    vec8 qf[DS];
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds)
+        qf[ds] = __builtin_bit_cast(vec8, ld_global_16(qp + (size_t)q_row * D + ds * 16 + half * 8));
+
+    const size_t kv_head = ((size_t)b * a.Hkv + g) * (size_t)a.kv_len;
+    const uint16_t* kp = static_cast<const uint16_t*>(a.k) + kv_head * D;
+    const uint16_t* vp = static_cast<const uint16_t*>(a.v) + kv_head * D;
+    const int last_key = a.kv_len - 1;
+
+    // ---- tile staging ------------------------------------------------------
+    u32x4 kreg[KCH];
+    u32x4 vreg[4];
+    const int v_kg = tid & 15;  // V: keys 4*v_kg .. +3 of the tile
+    const int v_dg = tid >> 4;  // V: dims 8*v_dg .. +7
+    // Position of key 4*c+e (c = v_kg & 3) inside its 16-key block of V^T:
+    // key 8*a + 4*h + e is stored at 8*h + 4*a + e, so that the 8 keys one
+    // lane half feeds to a 16-key MFMA step are contiguous.
+    const int v_pos = (v_kg >> 2) * 16 + 8 * (v_kg & 1) + 4 * ((v_kg >> 1) & 1);
+
+    auto load_tile = [&](int t0) {
+#pragma unroll
+        for (int j = 0; j < KCH; ++j) {
+            const int c = tid + 256 * j;
+            const int row = c / (D / 8), col = c % (D / 8);
+            const int key = min(t0 + row, last_key);
+            kreg[j] = ld_global_16(kp + (size_t)key * D + col * 8);
+        }
+        if (tid < VTHREADS) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = min(t0 + 4 * v_kg + r, last_key);
+                vreg[r] = ld_global_16(vp + (size_t)key * D + v_dg * 8);
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+        uint16_t* ks = smem + buf * (KT + VT);
+        uint16_t* vs = ks + KT;
+#pragma unroll
+        for (int j = 0; j < KCH; ++j) {
+            const int c = tid + 256 * j;
+            const int row = c / (D / 8), col = c % (D / 8);
+            *reinterpret_cast<u32x4*>(ks + row * KS + col * 8) = kreg[j];
+        }
+        if (tid < VTHREADS) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {  // dword e holds dims 8*v_dg + 2e, +1
+                u32x2 w0 = {pack_lo(vreg[0][e], vreg[1][e]), pack_lo(vreg[2][e], vreg[3][e])};
+                u32x2 w1 = {pack_hi(vreg[0][e], vreg[1][e]), pack_hi(vreg[2][e], vreg[3][e])};
+                *reinterpret_cast<u32x2*>(vs + (v_dg * 8 + 2 * e) * VS + v_pos) = w0;
+                *reinterpret_cast<u32x2*>(vs + (v_dg * 8 + 2 * e + 1) * VS + v_pos) = w1;
+            }
+        }
+    };
+
+    // ---- online softmax state (log2 domain: m is a max of s * c) ------------
+    float m = -INFINITY;
+    float l = 0.f;  // this lane's share of the row sum (its half of the keys)
+    f32x16 acc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+
+    if (n_tiles > 0) {
+        load_tile(0);
+        store_tile(0);
+    }
+    __syncthreads();
+
+    for (int it = 0; it < n_tiles; ++it) {
+        const int t0 = it * BN;
+        const int buf = it & 1;
+        if (it + 1 < n_tiles) load_tile(t0 + BN);
+
+        if (t0 < wave_kv_end) {  // wave-uniform: skip tiles this wave cannot see
+            const uint16_t* ks = smem + buf * (KT + VT);
+            const uint16_t* vs = ks + KT;
+
+            // S^T[key][query] for 64 keys (two 32-key halves)
+            f32x16 s[2];
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[kh][r] = 0.f;
+#pragma unroll
+                for (int ds = 0; ds < DS; ++ds) {
+                    vec8 ka = *reinterpret_cast<const vec8*>(ks + (kh * 32 + l32) * KS + ds * 16 + half * 8);
+                    s[kh] = mfma_32x32x16(ka, qf[ds], s[kh]);
+                }
+            }
+
+            if (t0 + BN > wave_full_end) {  // diagonal or tail tile: apply the mask
+                const int lim = CAUSAL ? min(my_q + a.delta + 1, a.kv_len) : a.kv_len;
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = t0 + kh * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                        if (key >= lim) s[kh][r] = -INFINITY;
+                    }
+            }
+
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kh][r]);
+            mx = fmaxf(mx, xor32(mx));
+            const float m_new = fmaxf(m, mx * a.c);
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            const float alpha = fast_exp2(m - m_use);
+            m = m_new;
+            l *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+
+            uint32_t pk[2][8];
+            float psum = 0.f;
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    const float p0 = fast_exp2(fmaf(s[kh][r], a.c, -m_use));
+                    const float p1 = fast_exp2(fmaf(s[kh][r + 1], a.c, -m_use));
+                    psum += p0 + p1;
+                    pk[kh][r >> 1] = pack2(TAG(), p0, p1);
+                }
+            l += psum;
+
+            // O^T[d][query] += V^T[d][key] P^T[key][query], 16 keys per step
+#pragma unroll
+            for (int k16 = 0; k16 < 4; ++k16) {
+                const int kh = k16 >> 1, base = (k16 & 1) * 4;
+                const u32x4 pw = {pk[kh][base], pk[kh][base + 1], pk[kh][base + 2], pk[kh][base + 3]};
+                const vec8 pb = __builtin_bit_cast(vec8, pw);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    vec8 va = *reinterpret_cast<const vec8*>(vs + (dt * 32 + l32) * VS + k16 * 16 + half * 8);
+                    acc[dt] = mfma_32x32x16(va, pb, acc[dt]);
+                }
+            }
+        }
+
+        if (it + 1 < n_tiles) store_tile(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2 -------------------
+    const float l_tot = l + xor32(l);
+    if (my_q < a.q_len) {
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        uint16_t* op = static_cast<uint16_t*>(a.o) + (q_head + my_q) * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d0 = dt * 32 + 8 * r4 + 4 * half;
+                const u32x2 w = {pack2(TAG(), acc[dt][4 * r4] * inv, acc[dt][4 * r4 + 1] * inv),
+                                 pack2(TAG(), acc[dt][4 * r4 + 2] * inv, acc[dt][4 * r4 + 3] * inv)};
+                *reinterpret_cast<u32x2*>(op + d0) = w;
+            }
+        if (half == 0)
+            a.lse[q_head + my_q] = l_tot > 0.f ? (m + fast_log2(l_tot)) * kLn2 : -INFINITY;
+    }
+}
+
+// fp32 inputs: the same schedule on v_mfma_f32_32x32x2f32 with fp32 softmax
+// weights (no rounding of P), one head per workgroup, 32-key tiles.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void prefill_fwd_f32(PrefillArgs a) {
+    constexpr int BN = 32;
+    constexpr int POS = 128;
+    constexpr int KS = D + 4;
+    constexpr int VS = D + 4;
+    constexpr int KT = BN * KS;
+    constexpr int VT = BN * VS;
+    constexpr int HD = D / 2;          // dims per lane half
+    constexpr int DT = D / 32;
+    constexpr int CH = BN * D / 4 / 256;  // 16-byte chunks per thread per tile (each of K, V)
+
+    __shared__ __attribute__((aligned(16))) float smem[2 * (KT + VT)];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int half = lane >> 5, l32 = lane & 31;
+
+    int pt = blockIdx.x / a.n_rest;
+    int rest = blockIdx.x - pt * a.n_rest;
+    if (CAUSAL) pt = a.n_pos_tiles - 1 - pt;
+    const int h = rest % a.Hq;
+    const int b = rest / a.Hq;
+    const int g = h / a.group;
+    const int wg_pos0 = pt * POS;
+    const int pos0 = wg_pos0 + wave * 32;
+    const int my_q = pos0 + l32;
+
+    int wg_kv_end = a.kv_len, wave_kv_end = a.kv_len, wave_full_end = a.kv_len;
+    if (CAUSAL) {
+        const int wg_last = min(wg_pos0 + POS, a.q_len) - 1;
+        wg_kv_end = max(0, min(a.kv_len, wg_last + a.delta + 1));
+        const int w_last = min(pos0 + 32, a.q_len) - 1;
+        wave_kv_end = pos0 < a.q_len ? max(0, min(a.kv_len, w_last + a.delta + 1)) : 0;
+        wave_full_end = max(0, min(a.kv_len, pos0 + a.delta + 1));
+    } else if (pos0 >= a.q_len) {
+        wave_kv_end = 0;
+    }
+    const int n_tiles = (wg_kv_end + BN - 1) / BN;
+
+    // Lane half `half` covers dims [half*HD, half*HD + HD); MFMA step j uses dim half*HD + j.
+    const size_t q_head = ((size_t)b * a.Hq + h) * (size_t)a.q_len;
+    const float* qp = static_cast<const float*>(a.q) + q_head * D;
+    const int q_row = min(my_q, a.q_len - 1);
+    float qf[HD];
+#pragma unroll
+    for (int j = 0; j < HD; j += 4) {
+        const f32x4 t = *reinterpret_cast<const f32x4*>(qp + (size_t)q_row * D + half * HD + j);
+        qf[j] = t[0]; qf[j + 1] = t[1]; qf[j + 2] = t[2]; qf[j + 3] = t[3];
+    }
+
+    const size_t kv_head = ((size_t)b * a.Hkv + g) * (size_t)a.kv_len;
+    const float* kp = static_cast<const float*>(a.k) + kv_head * D;
+    const float* vp = static_cast<const float*>(a.v) + kv_head * D;
+    const int last_key = a.kv_len - 1;
+
+    f32x4 kreg[CH], vreg[CH];
+    auto load_tile = [&](int t0) {
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const int c = tid + 256 * j;
+            const int row = c / (D / 4), col = c % (D / 4);
+            const int key = min(t0 + row, last_key);
+            kreg[j] = *reinterpret_cast<const f32x4*>(kp + (size_t)key * D + col * 4);
+            vreg[j] = *reinterpret_cast<const f32x4*>(vp + (size_t)key * D + col * 4);
+        }
+    };
+    auto store_tile = [&](int buf) {
+        float* ks = smem + buf * (KT + VT);
+        float* vs = ks + KT;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const int c = tid + 256 * j;
+            const int row = c / (D / 4), col = c % (D / 4);
+            *reinterpret_cast<f32x4*>(ks + row * KS + col * 4) = kreg[j];
+            *reinterpret_cast<f32x4*>(vs + row * VS + col * 4) = vreg[j];
+        }
+    };
+
+    float m = -INFINITY, l = 0.f;
+    f32x16 acc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+
+    if (n_tiles > 0) {
+        load_tile(0);
+        store_tile(0);
+    }
+    __syncthreads();
+
+    for (int it = 0; it < n_tiles; ++it) {
+        const int t0 = it * BN;
+        const int buf = it & 1;
+        if (it + 1 < n_tiles) load_tile(t0 + BN);
+        if (t0 < wave_kv_end) {
+            const float* ks = smem + buf * (KT + VT);
+            const float* vs = ks + KT;
+            f32x16 s;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[r] = 0.f;
+            const float* krow = ks + l32 * KS + half * HD;
+#pragma unroll
+            for (int j = 0; j < HD; j += 4) {
+                const f32x4 kv4 = *reinterpret_cast<const f32x4*>(krow + j);
+                s = mfma_32x32x2(kv4[0], qf[j], s);
+                s = mfma_32x32x2(kv4[1], qf[j + 1], s);
+                s = mfma_32x32x2(kv4[2], qf[j + 2], s);
+                s = mfma_32x32x2(kv4[3], qf[j + 3], s);
+            }
+            if (t0 + BN > wave_full_end) {
+                const int lim = CAUSAL ? min(my_q + a.delta + 1, a.kv_len) : a.kv_len;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = t0 + 8 * (r >> 2) + 4 * half + (r & 3);
+                    if (key >= lim) s[r] = -INFINITY;
+                }
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+            mx = fmaxf(mx, xor32(mx));
+            const float m_new = fmaxf(m, mx * a.c);
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            const float alpha = fast_exp2(m - m_use);
+            m = m_new;
+            l *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+            float p[16];
+            float psum = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                p[r] = fast_exp2(fmaf(s[r], a.c, -m_use));
+                psum += p[r];
+            }
+            l += psum;
+            // step r pairs key 8*(r/4) + 4*half + r%4 of lane half `half`
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = 8 * (r >> 2) + 4 * half + (r & 3);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+                    acc[dt] = mfma_32x32x2(vs[key * VS + dt * 32 + l32], p[r], acc[dt]);
+            }
+        }
+        if (it + 1 < n_tiles) store_tile(buf ^ 1);
+        __syncthreads();
+    }
+
+    const float l_tot = l + xor32(l);
+    if (my_q < a.q_len) {
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        float* op = static_cast<float*>(a.o) + (q_head + my_q) * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d0 = dt * 32 + 8 * r4 + 4 * half;
+                const f32x4 w = {acc[dt][4 * r4] * inv, acc[dt][4 * r4 + 1] * inv,
+                                 acc[dt][4 * r4 + 2] * inv, acc[dt][4 * r4 + 3] * inv};
+                *reinterpret_cast<f32x4*>(op + d0) = w;
+            }
+        if (half == 0)
+            a.lse[q_head + my_q] = l_tot > 0.f ? (m + fast_log2(l_tot)) * kLn2 : -INFINITY;
+    }
+}
+
+template <class TAG, int D, bool CAUSAL, int NH>
+hipError_t launch_mfma(PrefillArgs a, hipStream_t stream) {
+    constexpr int POS = 32 * (4 / NH);
+    a.n_pos_tiles = (a.q_len + POS - 1) / POS;
+    a.n_rest = a.B * a.Hkv * (a.group / NH);
+    const long long blocks = (long long)a.n_pos_tiles * a.n_rest;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((prefill_fwd_mfma<TAG, D, CAUSAL, NH>), dim3((unsigned)blocks), dim3(256), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+template <class TAG, int D, bool CAUSAL>
+hipError_t dispatch_nh(PrefillArgs a, hipStream_t stream) {
+    if (a.group % 4 == 0) return launch_mfma<TAG, D, CAUSAL, 4>(a, stream);
+    if (a.group % 2 == 0) return launch_mfma<TAG, D, CAUSAL, 2>(a, stream);
+    return launch_mfma<TAG, D, CAUSAL, 1>(a, stream);
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_f32(PrefillArgs a, hipStream_t stream) {
+    a.n_pos_tiles = (a.q_len + 127) / 128;
+    a.n_rest = a.B * a.Hq;
+    const long long blocks = (long long)a.n_pos_tiles * a.n_rest;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((prefill_fwd_f32<D, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <class TAG>
+hipError_t dispatch_d(PrefillArgs a, int D, bool causal, hipStream_t stream) {
+    if (D == 64) return causal ? dispatch_nh<TAG, 64, true>(a, stream) : dispatch_nh<TAG, 64, false>(a, stream);
+    return causal ? dispatch_nh<TAG, 128, true>(a, stream) : dispatch_nh<TAG, 128, false>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_prefill(PrefillArgs a, int D, bool causal, int dtype, hipStream_t stream) {
+    switch (dtype) {
+    case kDtypeBF16: return dispatch_d<bf16_tag>(a, D, causal, stream);
+    case kDtypeF16: return dispatch_d<f16_tag>(a, D, causal, stream);
+    default:
+        if (D == 64) return causal ? launch_f32<64, true>(a, stream) : launch_f32<64, false>(a, stream);
+        return causal ? launch_f32<128, true>(a, stream) : launch_f32<128, false>(a, stream);
+    }
+}
+
+}  // namespace gqa

@@ -1,0 +1,144 @@
+/*
+ * gqa_attn.h - C ABI of the MI355X (gfx950) GQA attention forward library.
+ *
+ * Two operations, both the forward pass of softmax attention with grouped
+ * query heads:
+ *
+ *   attn_fwd            prefill / general forward, FlashAttention style
+ *                       (causal_forward_kernel.py, `_flash_attention_forward_gqa_kernel`
+ *                       and its wrapper `flash_attention_forward`).
+ *   attn_decode_splitk  one query per sequence against a (paged) KV cache,
+ *                       split along the keys and merged through the
+ *                       per-chunk log-sum-exp (splitk_kernels.py,
+ *                       `_fwd_kernel_splitK` and `_splitK_reduce`).
+ *
+ * What is computed, for batch b, query head h, query row i:
+ *   g      = h / (Hq / Hkv)                       (query head -> K/V head)
+ *   s_j    = scale * <q[b,h,i,:], k[b,g,j,:]>
+ *   vis(i) = { j < kv_len : !causal || j <= i + (kv_len - q_len) }
+ *            (bottom-right aligned causal mask, as in the FlashInfer-style
+ *             prefill page gpt-o3 / triton6fd1ef, `_gqa_prefill_kernel`)
+ *   lse    = log( sum_{j in vis(i)} exp(s_j) )    (natural log, scale included)
+ *   o      = sum_{j in vis(i)} exp(s_j - lse) * v[b,g,j,:]
+ * A row with no visible key gets o = 0 and lse = -inf (the zero-fill rule of
+ * `_fwd_kernel_splitK`).  Accumulation is in fp32; o is rounded to nearest
+ * even into the input dtype; lse is fp32.  For fp16/bf16 inputs the softmax
+ * weights are rounded to the input dtype before the P.V product, as in both
+ * the causal_forward_kernel.py and splitk_kernels.py kernels.
+ *
+ * Conventions shared by every call:
+ *   - Every pointer is a DEVICE pointer owned by the caller.  The library
+ *     allocates, frees and synchronises nothing; it only enqueues kernels.
+ *   - Work is ordered on `hip_stream` (a hipStream_t; NULL = default stream)
+ *     and is asynchronous: outputs are valid once the stream reaches it.
+ *   - Arguments are validated before any launch; on error nothing is
+ *     launched and outputs are untouched.  No exception crosses the ABI.
+ *   - Outputs must not alias inputs.
+ *   - Tensors are contiguous, row-major, in the layouts given per call.
+ *   - The library holds no mutable global state; calls from several host
+ *     threads on different streams are safe.
+ */
+#ifndef GQA_ATTN_H
+#define GQA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GQA_F32 = 0,   /* IEEE binary32 */
+    GQA_F16 = 1,   /* IEEE binary16 */
+    GQA_BF16 = 2   /* bfloat16 */
+} gqa_dtype_t;
+
+typedef enum {
+    GQA_OK = 0,
+    GQA_ERR_INVALID_ARG = 1,  /* null pointer, bad size or geometry */
+    GQA_ERR_UNSUPPORTED = 2,  /* valid request with no instantiated kernel (e.g. D not in {64,128}) */
+    GQA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than attn_decode_workspace_bytes() */
+    GQA_ERR_HIP = 4           /* the HIP runtime reported an error at launch */
+} gqa_status_t;
+
+/*
+ * attn_fwd - attention forward (prefill, or any q_len).
+ *
+ *   q   [B, Hq,  q_len,  D]  dtype        (read)
+ *   k   [B, Hkv, kv_len, D]  dtype        (read)
+ *   v   [B, Hkv, kv_len, D]  dtype        (read)
+ *   o   [B, Hq,  q_len,  D]  dtype        (written)
+ *   lse [B, Hq,  q_len]      float32      (written; natural-log LSE)
+ *
+ * Requirements: B, q_len, kv_len >= 0; Hq, Hkv > 0; Hq % Hkv == 0 (the group
+ * divisibility check of `flash_attention_forward`); D in {64, 128}; scale
+ * finite (the usual value is 1/sqrt(D)).  dtype F32 runs an fp32 path with
+ * fp32 softmax weights; F16/BF16 run the matrix-core path.
+ * causal != 0 applies the bottom-right mask above; with q_len == kv_len it is
+ * the usual lower-triangular mask.
+ * B == 0 or q_len == 0: nothing to do, returns GQA_OK.
+ * kv_len == 0 (or causal rows before the offset): o = 0, lse = -inf.
+ * Returns GQA_ERR_INVALID_ARG / GQA_ERR_UNSUPPORTED / GQA_ERR_HIP or GQA_OK.
+ */
+gqa_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int Hq, int Hkv, int q_len, int kv_len, int D,
+                      float scale, int causal, gqa_dtype_t dtype, void* hip_stream);
+
+/*
+ * attn_decode_workspace_bytes - device workspace attn_decode_splitk needs:
+ * B * Hq * n_splits * (D + 1) * 4 bytes (per-chunk fp32 outputs and LSEs).
+ * Returns 0 for non-positive arguments.
+ */
+size_t attn_decode_workspace_bytes(int B, int Hq, int D, int n_splits);
+
+/*
+ * attn_decode_splitk - single-query attention per sequence, split-K.
+ *
+ *   q           [B, Hq, D]         dtype    (read; one query per sequence and head)
+ *   o           [B, Hq, D]         dtype    (written)
+ *   lse         [B, Hq]            float32  (written; natural log)
+ *   seq_lens    [B]                int32    (read; 0 <= seq_lens[b] <= max_kv_len)
+ *   block_table != NULL: paged KV cache
+ *       k, v        [num_pages, page_size, Hkv, D] dtype
+ *       block_table [B, max_pages_per_seq] int32; token t of sequence b lives in
+ *                   page block_table[b * max_pages_per_seq + t / page_size],
+ *                   row t % page_size (the paged branch of `_fwd_kernel_splitK`).
+ *       page_size must be a power of two; max_pages_per_seq * page_size >= max_kv_len.
+ *   block_table == NULL: dense cache
+ *       k, v        [B, Hkv, max_kv_len, D] dtype; rows >= seq_lens[b] are ignored.
+ *       page_size and max_pages_per_seq are ignored.
+ *   workspace   >= attn_decode_workspace_bytes(B, Hq, D, n_splits) bytes of device
+ *               memory, 16-byte aligned, used as scratch for the per-chunk
+ *               results; its contents before and after the call are unspecified.
+ *
+ * Sequence b is cut into n_splits chunks of ceil(ceil(seq_lens[b]/n_splits)/64)*64
+ * tokens (trailing chunks may be empty); each chunk yields a partial output and
+ * its LSE, and a second kernel merges the chunks with weights exp(lse_s - max)
+ * (`_splitK_reduce`).  The result does not depend on n_splits beyond rounding.
+ * seq_lens[b] == 0 gives o = 0, lse = -inf.
+ *
+ * The contents of seq_lens and block_table are trusted: they are not
+ * bounds-checked on the device, and an out-of-range page id or length is
+ * undefined behaviour (the split-K page loads its block table unchecked too).
+ *
+ * Requirements: B >= 0, Hq, Hkv > 0, Hq % Hkv == 0, Hq / Hkv <= 8,
+ * D in {64, 128}, dtype F16 or BF16, 1 <= n_splits <= 256, max_kv_len >= 0.
+ * B == 0 returns GQA_OK without launching.
+ */
+gqa_status_t attn_decode_splitk(const void* q, const void* k, const void* v, void* o, float* lse,
+                                const int* seq_lens, const int* block_table,
+                                int max_pages_per_seq, int page_size,
+                                int B, int Hq, int Hkv, int D, int max_kv_len,
+                                float scale, int n_splits,
+                                void* workspace, size_t workspace_bytes,
+                                gqa_dtype_t dtype, void* hip_stream);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* attn_status_str(gqa_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_ATTN_H */

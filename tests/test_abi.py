@@ -1,0 +1,112 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments with the documented status codes
+before launching anything.  No call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gqa_attention_forward_attn_amd as gqa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa_attn.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIP = 0, 1, 2, 3, 4
+BF16, F16, F32 = gqa.GQA_BF16, gqa.GQA_F16, gqa.GQA_F32
+# Fake, 256-byte aligned device addresses: validation rejects every call
+# below before any pointer is used.
+P = [ctypes.c_void_p(0x10000 * (i + 1)) for i in range(8)]
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"if", "sizeof"})
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(gqa.LIB_PATH):
+        pytest.fail("libgqa_attn.so is not built (run __graft_entry__.build())")
+    return gqa.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) == set(gqa.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in gqa_attn.h but not exported"
+
+
+def test_status_strings(L):
+    for code in range(5):
+        s = L.attn_status_str(code).decode()
+        assert s.startswith(gqa.STATUS[code])
+    assert L.attn_status_str(99).decode().startswith("unknown")
+
+
+def test_workspace_bytes(L):
+    assert L.attn_decode_workspace_bytes(16, 32, 128, 16) == 16 * 32 * 16 * 129 * 4
+    assert L.attn_decode_workspace_bytes(0, 32, 128, 16) == 0
+    assert L.attn_decode_workspace_bytes(1, 1, 64, 0) == 0
+
+
+def fwd(L, B=1, Hq=4, Hkv=2, q_len=8, kv_len=8, D=64, scale=0.125, causal=1, dtype=BF16,
+        q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4]):
+    return L.attn_fwd(q, k, v, o, lse, B, Hq, Hkv, q_len, kv_len, D, scale, causal, dtype, None)
+
+
+def test_fwd_validation(L):
+    assert fwd(L, Hq=6, Hkv=4) == INVALID          # Hq % Hkv
+    assert fwd(L, Hkv=0) == INVALID
+    assert fwd(L, B=-1) == INVALID
+    assert fwd(L, q_len=-3) == INVALID
+    assert fwd(L, kv_len=-1) == INVALID
+    assert fwd(L, scale=float("nan")) == INVALID
+    assert fwd(L, scale=0.0) == INVALID
+    assert fwd(L, dtype=7) == INVALID
+    assert fwd(L, D=96) == UNSUPPORTED
+    assert fwd(L, D=256) == UNSUPPORTED
+    assert fwd(L, q=None) == INVALID
+    assert fwd(L, lse=None) == INVALID
+    assert fwd(L, k=None) == INVALID
+    assert fwd(L, q=ctypes.c_void_p(0x10008)) == INVALID   # misaligned
+    # nothing to do: returns OK without launching
+    assert fwd(L, B=0) == OK
+    assert fwd(L, q_len=0) == OK
+
+
+def dec(L, B=2, Hq=8, Hkv=2, D=128, max_kv_len=512, n_splits=4, page_size=256, max_pages=2,
+        bt=P[6], ws=P[7], ws_bytes=None, dtype=BF16, scale=0.1, q=P[0], seq=P[5]):
+    if ws_bytes is None:
+        ws_bytes = L.attn_decode_workspace_bytes(B, Hq, D, n_splits)
+    return L.attn_decode_splitk(q, P[1], P[2], P[3], P[4], seq, bt, max_pages, page_size,
+                                B, Hq, Hkv, D, max_kv_len, scale, n_splits, ws, ws_bytes,
+                                dtype, None)
+
+
+def test_decode_validation(L):
+    assert dec(L, Hq=6, Hkv=4) == INVALID
+    assert dec(L, n_splits=0) == INVALID
+    assert dec(L, n_splits=257) == INVALID
+    assert dec(L, page_size=96) == INVALID             # not a power of two
+    assert dec(L, page_size=0) == INVALID
+    assert dec(L, max_pages=1) == INVALID              # 1 * 256 < max_kv_len
+    assert dec(L, scale=-1.0) == INVALID
+    assert dec(L, max_kv_len=-1) == INVALID
+    assert dec(L, D=80) == UNSUPPORTED
+    assert dec(L, dtype=F32) == UNSUPPORTED
+    assert dec(L, Hq=32, Hkv=2) == UNSUPPORTED         # group of 16
+    assert dec(L, q=None) == INVALID
+    assert dec(L, seq=None) == INVALID
+    assert dec(L, ws=None) == WORKSPACE
+    assert dec(L, ws_bytes=100) == WORKSPACE
+    assert dec(L, B=0) == OK
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        gqa.attn_fwd(q, q[:, :1].contiguous(), q[:, :1].contiguous())

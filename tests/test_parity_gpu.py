@@ -1,0 +1,257 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Tolerances (max abs error over the compared elements):
+  fp32 inputs         O and LSE within 1e-5
+  bf16 / fp16 inputs  O within 2e-2, LSE within 1e-3
+A -inf LSE must be -inf on both sides and no NaN may appear anywhere.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import gqa_attention_forward_attn_amd as gqa
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": (1e-5, 1e-5), "bf16": (2e-2, 1e-3), "f16": (2e-2, 1e-3)}
+DTNAME = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16"}
+
+
+def check(o_gpu, lse_gpu, o_ref, lse_ref, dtname, what=""):
+    o_gpu = np.asarray(o_gpu, dtype=np.float64)
+    lse_gpu = np.asarray(lse_gpu, dtype=np.float64)
+    tol_o, tol_l = TOL[dtname]
+    assert not np.isnan(o_gpu).any(), f"{what}: NaN in O"
+    assert not np.isnan(lse_gpu).any(), f"{what}: NaN in LSE"
+    err_o = np.abs(o_gpu - o_ref).max() if o_ref.size else 0.0
+    assert err_o <= tol_o, f"{what}: max |O - oracle| = {err_o:.3e} > {tol_o}"
+    ninf_ref = np.isneginf(lse_ref)
+    assert np.array_equal(ninf_ref, np.isneginf(lse_gpu)), f"{what}: -inf LSE pattern differs"
+    fin = ~ninf_ref
+    err_l = np.abs(lse_gpu[fin] - lse_ref[fin]).max() if fin.any() else 0.0
+    assert err_l <= tol_l, f"{what}: max |LSE - oracle| = {err_l:.3e} > {tol_l}"
+    return err_o, err_l
+
+
+def gpu_fwd(q, k, v, causal, scale, canary=True):
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    out = torch.full_like(qd, float("nan")) if canary else None
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device="cuda") if canary else None
+    o, l = gqa.attn_fwd(qd, kd, vd, causal=causal, scale=scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return o, l
+
+
+# ---- prefill: every element, several tiles and ragged tails ----------------
+
+SMALL = [
+    # B, Hq, Hkv, q_len, kv_len, D, dtype, causal
+    (1, 4, 2, 128, 128, 64, "f32", True),
+    (2, 4, 2, 200, 200, 64, "f32", False),
+    (1, 2, 1, 70, 300, 128, "f32", True),
+    (2, 8, 2, 200, 200, 128, "bf16", True),
+    (1, 8, 8, 130, 333, 64, "f16", False),
+    (1, 8, 1, 77, 300, 128, "bf16", True),     # bottom-right offset, G = 8
+    (2, 4, 2, 300, 100, 64, "bf16", True),     # q_len > kv_len: leading rows empty
+    (1, 2, 2, 1, 517, 128, "bf16", True),      # single query row
+    (1, 6, 3, 257, 257, 128, "f16", True),     # G = 2
+    (3, 4, 4, 65, 1, 64, "bf16", False),       # one key
+    (1, 32, 4, 96, 416, 128, "bf16", True),    # G = 8 with offset
+    (1, 12, 4, 64, 64, 64, "f16", True),       # G = 3
+]
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "-".join(map(str, s)))
+def test_prefill_all_elements(shape):
+    B, Hq, Hkv, Lq, Lk, D, dt, causal = shape
+    print(f"prefill case {shape}", flush=True)
+    q, k, v = W.make_prefill(B, Hq, Hkv, Lq, Lk, D, dt, seed=sum(shape[:6]))
+    scale = W.fp32_scale(D)
+    o, l = gpu_fwd(q, k, v, causal, scale)
+    o_ref, l_ref = oracle.attn_fwd(q, k, v, scale, causal)
+    check(o.double().cpu().numpy(), l.double().cpu().numpy(), o_ref, l_ref, dt, str(shape))
+
+
+def test_prefill_kv_len_zero():
+    q = torch.randn(1, 4, 16, 64).to(torch.bfloat16)
+    k = torch.zeros(1, 2, 0, 64, dtype=torch.bfloat16)
+    o, l = gpu_fwd(q, k, k.clone(), False, 0.125)
+    assert torch.all(o.float() == 0) and torch.all(torch.isneginf(l))
+
+
+# ---- prefill at the workload sizes: sampled rows ---------------------------
+
+def sample_rows(B, Hq, Lq, n_random, seed):
+    """Rows that always include the first/last positions and tile edges of every
+    head, plus random positions."""
+    g = np.random.default_rng(seed)
+    pos = {0, 1, 31, 32, 63, 64, 127, 128, Lq // 2, Lq - 2, Lq - 1}
+    pos = sorted(p for p in pos if 0 <= p < Lq)
+    rows = []
+    for b in range(B):
+        for h in range(Hq):
+            base = (b * Hq + h) * Lq
+            rows.extend(base + p for p in pos)
+    rows.extend(g.integers(0, B * Hq * Lq, size=n_random).tolist())
+    return np.unique(np.array(rows, dtype=np.int64))
+
+
+@pytest.mark.parametrize("spec", W.PREFILL_WORKLOADS, ids=lambda s: s.name)
+def test_prefill_workload_sampled(spec):
+    print(f"workload {spec.name}", flush=True)
+    q, k, v = W.make_prefill_spec(spec)
+    scale = W.fp32_scale(spec.D)
+    o, l = gpu_fwd(q, k, v, spec.causal, scale)
+    o = o.double().cpu().numpy().reshape(-1, spec.D)
+    l = l.double().cpu().numpy().reshape(-1)
+    # properties at every row: finite (every row here sees at least one key)
+    assert np.isfinite(o).all() and np.isfinite(l).all()
+    rows = sample_rows(spec.B, spec.Hq, spec.q_len, 1024, spec.seed)
+    o_ref, l_ref = oracle.attn_fwd(q, k, v, scale, spec.causal, rows=rows)
+    e_o, e_l = check(o[rows], l[rows], o_ref, l_ref, spec.dtype, spec.name)
+    print(f"{spec.name}: rows={len(rows)} max|dO|={e_o:.3e} max|dLSE|={e_l:.3e}")
+
+
+def test_causal_row_zero_exact():
+    # delta = 0: row 0 sees key 0 only, so P = 1 and O[0] = V[0] bit for bit.
+    spec = W.CAUSAL_GQA_PREFILL
+    q, k, v = W.make_prefill_spec(spec)
+    o, l = gpu_fwd(q, k, v, True, W.fp32_scale(spec.D))
+    G = spec.Hq // spec.Hkv
+    v_rep = v.repeat_interleave(G, dim=1)
+    assert torch.equal(o[:, :, 0].cpu(), v_rep[:, :, 0])
+
+
+def test_identity_values_expose_probabilities():
+    # V = I (kv_len <= D): O rows are the softmax rows P.
+    Lq, Lk, D = 100, 128, 128
+    q, k, _ = W.make_prefill(1, 4, 1, Lq, Lk, D, "bf16", seed=77)
+    v = torch.eye(Lk, D).view(1, 1, Lk, D).to(torch.bfloat16)
+    o, _ = gpu_fwd(q, k, v, True, W.fp32_scale(D))
+    o = o.double().cpu().numpy()
+    for h in range(4):
+        p = oracle.softmax_matrix(q, k, W.fp32_scale(D), True, 0, h)
+        assert np.abs(o[0, h] - p).max() <= 2e-2
+        np.testing.assert_allclose(o[0, h].sum(axis=1), 1.0, atol=2e-2)
+
+
+def test_deterministic():
+    q, k, v = W.make_prefill(2, 8, 2, 300, 300, 128, "bf16", seed=3)
+    o1, l1 = gpu_fwd(q, k, v, True, 0.1)
+    o2, l2 = gpu_fwd(q, k, v, True, 0.1)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_large_scores_stable():
+    q, k, v = W.make_prefill(1, 4, 2, 130, 130, 64, "bf16", seed=9)
+    q = (q.float() * 30).to(torch.bfloat16)  # scores of order 100s
+    scale = W.fp32_scale(64)
+    o, l = gpu_fwd(q, k, v, True, scale)
+    o_ref, l_ref = oracle.attn_fwd(q, k, v, scale, True)
+    check(o.double().cpu().numpy(), l.double().cpu().numpy(), o_ref, l_ref, "bf16", "x30")
+
+
+# ---- decode -----------------------------------------------------------------
+
+def gpu_decode(inp, n_splits, scale, paged=True):
+    q = inp.q.cuda()
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full(q.shape[:2], float("nan"), dtype=torch.float32, device="cuda")
+    if paged:
+        o, l = gqa.attn_decode_splitk(q, inp.k_cache.cuda(), inp.v_cache.cuda(), inp.seq_lens.cuda(),
+                                      block_table=inp.block_table.cuda(), n_splits=n_splits,
+                                      scale=scale, max_kv_len=inp.max_kv_len, out=out, lse=lse)
+    else:
+        o, l = gqa.attn_decode_splitk(q, inp.k_dense.cuda(), inp.v_dense.cuda(), inp.seq_lens.cuda(),
+                                      n_splits=n_splits, scale=scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return o.double().cpu().numpy(), l.double().cpu().numpy()
+
+
+def test_decode_workload_all_rows():
+    spec = W.PAGED_DECODE
+    print("workload paged_decode", flush=True)
+    inp = W.make_decode_spec(spec)
+    scale = W.fp32_scale(spec.D)
+    o, l = gpu_decode(inp, spec.n_splits, scale)
+    o_ref, l_ref = oracle.attn_decode(inp.q, inp.k_cache, inp.v_cache, inp.seq_lens, scale,
+                                      block_table=inp.block_table, max_kv_len=inp.max_kv_len)
+    e_o, e_l = check(o, l, o_ref, l_ref, "bf16", "paged_decode")
+    print(f"paged_decode: max|dO|={e_o:.3e} max|dLSE|={e_l:.3e}")
+
+
+DECODE = [
+    # B, Hq, Hkv, D, dtype, len_lo, len_hi, page_size, n_splits
+    (4, 32, 8, 128, "bf16", 1, 700, 256, 16),
+    (3, 8, 8, 64, "f16", 1, 300, 16, 3),
+    (2, 16, 2, 128, "bf16", 100, 2000, 64, 64),     # G = 8
+    (5, 4, 2, 128, "f16", 1, 63, 1, 1),             # page size 1, one split
+    (2, 6, 3, 64, "bf16", 500, 900, 128, 7),        # G = 2
+]
+
+
+@pytest.mark.parametrize("case", DECODE, ids=lambda c: "-".join(map(str, c)))
+def test_decode_cases(case):
+    B, Hq, Hkv, D, dt, lo, hi, ps, ns = case
+    print(f"decode case {case}", flush=True)
+    inp = W.make_decode(B, Hq, Hkv, D, dt, seed=sum(case[:4]) + hi, len_lo=lo, len_hi=hi, page_size=ps)
+    scale = W.fp32_scale(D)
+    o, l = gpu_decode(inp, ns, scale)
+    o_ref, l_ref = oracle.attn_decode(inp.q, inp.k_cache, inp.v_cache, inp.seq_lens, scale,
+                                      block_table=inp.block_table, max_kv_len=inp.max_kv_len)
+    check(o, l, o_ref, l_ref, dt, str(case))
+
+
+def test_decode_empty_and_short_sequences():
+    inp = W.make_decode(4, 8, 2, 128, "bf16", seed=5, seq_lens=[0, 1, 64, 65], page_size=64, max_pages=2)
+    inp.block_table[0, 0] = 0  # never read for an empty sequence
+    o, l = gpu_decode(inp, 16, 0.09)
+    o_ref, l_ref = oracle.attn_decode(inp.q, inp.k_cache, inp.v_cache, inp.seq_lens, 0.09,
+                                      block_table=inp.block_table, max_kv_len=inp.max_kv_len)
+    check(o, l, o_ref, l_ref, "bf16", "empty/short")
+    assert np.all(o[0] == 0) and np.all(np.isneginf(l[0]))
+
+
+def test_decode_split_count_invariance():
+    inp = W.make_decode(3, 16, 4, 128, "bf16", seed=6, len_lo=200, len_hi=3000, page_size=256)
+    res = [gpu_decode(inp, ns, 0.088) for ns in (1, 2, 5, 16, 64)]
+    o_ref, l_ref = oracle.attn_decode(inp.q, inp.k_cache, inp.v_cache, inp.seq_lens, 0.088,
+                                      block_table=inp.block_table, max_kv_len=inp.max_kv_len)
+    for o, l in res:
+        check(o, l, o_ref, l_ref, "bf16", "split invariance")
+
+
+def test_decode_page_permutation_bitwise():
+    kw = dict(B=3, Hq=8, Hkv=2, D=128, dtype="bf16", seed=8, len_lo=300, len_hi=900, page_size=64)
+    a = W.make_decode(**kw, permute=True)
+    b = W.make_decode(**kw, permute=False)
+    ka = torch.empty_like(a.k_cache)
+    va = torch.empty_like(a.v_cache)
+    for s in range(3):
+        n = (int(a.seq_lens[s]) + 63) // 64
+        ka[a.block_table[s, :n].long()] = b.k_cache[b.block_table[s, :n].long()]
+        va[a.block_table[s, :n].long()] = b.v_cache[b.block_table[s, :n].long()]
+    a.k_cache, a.v_cache = ka, va
+    o1, l1 = gpu_decode(a, 16, 0.1)
+    o2, l2 = gpu_decode(b, 16, 0.1)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_decode_dense_matches_paged():
+    inp = W.make_decode(3, 8, 2, 64, "f16", seed=10, len_lo=10, len_hi=500, page_size=32)
+    L = inp.max_kv_len
+    kd = torch.zeros(3, 2, L, 64, dtype=torch.float16)
+    vd = torch.zeros(3, 2, L, 64, dtype=torch.float16)
+    for s in range(3):
+        n = int(inp.seq_lens[s])
+        pages = inp.block_table[s, :(n + 31) // 32].long()
+        kd[s, :, :n] = inp.k_cache[pages].reshape(-1, 2, 64)[:n].permute(1, 0, 2)
+        vd[s, :, :n] = inp.v_cache[pages].reshape(-1, 2, 64)[:n].permute(1, 0, 2)
+    inp.k_dense, inp.v_dense = kd, vd
+    o1, l1 = gpu_decode(inp, 4, 0.125, paged=True)
+    o2, l2 = gpu_decode(inp, 4, 0.125, paged=False)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    o_ref, l_ref = oracle.attn_decode(inp.q, kd, vd, inp.seq_lens, 0.125)
+    check(o2, l2, o_ref, l_ref, "f16", "dense")
