@@ -1,0 +1,259 @@
+"""Benchmark: GQA attention forward on one MI355X.
+
+Prints ONE JSON line.  The headline workload is causal GQA prefill in bf16
+(B=2, Hq=32, Hkv=8, S=2048, D=128): one step is one attn_fwd call over that
+batch, inputs already resident in HBM.  `value` is TFLOP/s counted on the
+visible (query, key) pairs only (4*D flop per pair; masked work is not
+credited).  The other workloads (fp32 correctness shape, bottom-right offset
+prefill, non-causal fp16 MHA, split-K paged decode) are timed the same way and
+reported under "workloads".
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--only NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import gqa_attention_forward_attn_amd as gqa  # noqa: E402
+import workloads as W  # noqa: E402
+
+PEAK_MFMA_16BIT_TFLOPS = 2516.6   # MI355X dense bf16/fp16 MFMA (2.5 PFLOP/s published)
+PEAK_MFMA_F32_TFLOPS = 157.3      # MI355X fp32 MFMA
+PEAK_HBM_GBPS = 8000.0            # MI355X HBM3E
+
+PRIMARY = W.CAUSAL_GQA_PREFILL
+METRIC = "attention fwd TFLOP/s + % bf16 MFMA peak; decode GB/s + % HBM peak"
+
+# HBM traffic per launch of the dominant kernel from rocprofv3 --pmc
+# (FETCH_SIZE, WRITE_SIZE, KiB per dispatch), scaled by the same counters on a
+# copy of known size; None until counters are taken for the current kernel.
+MEASURED_TRAFFIC_BYTES = None
+
+
+def visible_pairs(q_len: int, kv_len: int, causal: bool) -> int:
+    if not causal:
+        return q_len * kv_len
+    delta = kv_len - q_len
+    return int(sum(max(0, min(kv_len, i + 1 + delta)) for i in range(q_len)))
+
+
+def prefill_flops(spec) -> int:
+    return 4 * spec.D * spec.B * spec.Hq * visible_pairs(spec.q_len, spec.kv_len, spec.causal)
+
+
+def decode_bytes(spec, inp) -> int:
+    elt = 2
+    tokens = int(inp.seq_lens.to(torch.int64).sum())
+    pages = int(sum((int(s) + spec.page_size - 1) // spec.page_size for s in inp.seq_lens))
+    kv = 2 * tokens * spec.Hkv * spec.D * elt
+    qo = 2 * spec.B * spec.Hq * spec.D * elt
+    lse = spec.B * spec.Hq * 4
+    meta = 4 * pages + 4 * spec.B
+    return kv + qo + lse + meta
+
+
+def time_launches(fn, steps: int, warmup: int):
+    """Warm up, then time `steps` calls: wall time around the whole loop
+    (synchronize on both sides) and a HIP event pair around every call on the
+    stream the library launches on (torch's current stream)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]) * 1e-3
+    return wall, per
+
+
+def bench_prefill(spec, steps, warmup):
+    q, k, v = W.make_prefill_spec(spec)
+    dev = torch.device("cuda:0")
+    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    scale = W.fp32_scale(spec.D)
+
+    def step():
+        gqa.attn_fwd(q, k, v, causal=spec.causal, scale=scale, out=o, lse=lse)
+
+    wall, per = time_launches(step, steps, warmup)
+    flops = prefill_flops(spec)
+    peak = PEAK_MFMA_F32_TFLOPS if spec.dtype == "f32" else PEAK_MFMA_16BIT_TFLOPS
+    kern_s = float(np.mean(per))
+    return {
+        "workload": spec.name, "dtype": spec.dtype, "causal": spec.causal,
+        "shape": {"B": spec.B, "Hq": spec.Hq, "Hkv": spec.Hkv, "q_len": spec.q_len,
+                  "kv_len": spec.kv_len, "D": spec.D},
+        "flop_per_launch": flops,
+        "ms_per_step": wall / steps * 1e3,
+        "kernel_ms_mean": kern_s * 1e3, "kernel_ms_min": float(per.min()) * 1e3,
+        "kernel_ms_p90": float(np.percentile(per, 90)) * 1e3,
+        "tflops": flops * steps / wall / 1e12,
+        "kernel_tflops": flops / kern_s / 1e12,
+        "peak_tflops": peak,
+        "frac_of_peak": flops / kern_s / 1e12 / peak,
+    }
+
+
+def bench_decode(spec, steps, warmup):
+    inp = W.make_decode_spec(spec)
+    dev = torch.device("cuda:0")
+    q = inp.q.to(dev)
+    kc, vc = inp.k_cache.to(dev), inp.v_cache.to(dev)
+    sl, bt = inp.seq_lens.to(dev), inp.block_table.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    ws = torch.empty(gqa.decode_workspace_bytes(spec.B, spec.Hq, spec.D, spec.n_splits),
+                     dtype=torch.uint8, device=dev)
+    scale = W.fp32_scale(spec.D)
+
+    def step():
+        gqa.attn_decode_splitk(q, kc, vc, sl, block_table=bt, n_splits=spec.n_splits, scale=scale,
+                               max_kv_len=inp.max_kv_len, workspace=ws, out=o, lse=lse)
+
+    wall, per = time_launches(step, steps, warmup)
+    nbytes = decode_bytes(spec, inp)
+    kern_s = float(np.mean(per))
+    return {
+        "workload": spec.name, "dtype": spec.dtype,
+        "shape": {"B": spec.B, "Hq": spec.Hq, "Hkv": spec.Hkv, "D": spec.D,
+                  "page_size": spec.page_size, "n_splits": spec.n_splits,
+                  "sum_kv_len": int(inp.seq_lens.to(torch.int64).sum())},
+        "bytes_per_step": nbytes,
+        "workspace_bytes_rw": 2 * spec.B * spec.Hq * spec.n_splits * (spec.D + 1) * 4,
+        "ms_per_step": wall / steps * 1e3,
+        "kernel_ms_mean": kern_s * 1e3, "kernel_ms_min": float(per.min()) * 1e3,
+        "gbps": nbytes * steps / wall / 1e9,
+        "kernel_gbps": nbytes / kern_s / 1e9,
+        "peak_gbps": PEAK_HBM_GBPS,
+        "frac_of_peak": nbytes / kern_s / 1e9 / PEAK_HBM_GBPS,
+    }
+
+
+def cpu_baseline(spec, target_s=12.0):
+    """The oracle, as it stands, on an evenly spaced sample of rows of the
+    workload; rate in TFLOP/s on the same visible-pair flop count."""
+    import oracle
+    q, k, v = W.make_prefill_spec(spec)
+    scale = W.fp32_scale(spec.D)
+    total = spec.B * spec.Hq * spec.q_len
+    delta = spec.kv_len - spec.q_len
+
+    def run(n):
+        rows = np.linspace(0, total - 1, n).astype(np.int64)
+        pos = rows % spec.q_len
+        vis = np.minimum(spec.kv_len, np.maximum(0, pos + 1 + delta)) if spec.causal else \
+            np.full_like(pos, spec.kv_len)
+        t0 = time.perf_counter()
+        oracle.attn_fwd(q, k, v, scale, spec.causal, rows=rows)
+        dt = time.perf_counter() - t0
+        return dt, int(4 * spec.D * vis.sum())
+
+    probe_n = 512
+    dt, _ = run(probe_n)
+    n = int(min(total, max(probe_n, probe_n * target_s / max(dt, 1e-3))))
+    dt, flops = run(n)
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{n} of {total} query rows of {spec.name} (evenly spaced), fp64, "
+                  f"{dt:.1f} s on {oracle.num_threads()} OpenMP threads ({platform.processor() or 'host CPU'})",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default=None, help="time only this workload (profiling runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build measures one GPU; run with --gpus 1 "
+                                   "(the multi-GPU sharding is described in DESIGN.md, not built)"}))
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(2)
+
+    all_specs = [W.CAUSAL_GQA_FP32, W.CAUSAL_GQA_PREFILL, W.CAUSAL_GQA_OFFSET,
+                 W.MHA_NONCAUSAL_FP16, W.PAGED_DECODE]
+    if args.only:
+        specs = [s for s in all_specs if s.name == args.only]
+        if not specs:
+            sys.exit(f"unknown workload {args.only}")
+        for s in specs:
+            r = bench_decode(s, args.steps, args.warmup) if isinstance(s, W.DecodeSpec) else \
+                bench_prefill(s, args.steps, args.warmup)
+            print(json.dumps(r), flush=True)
+        return
+
+    results = {}
+    for s in all_specs:
+        if s is PRIMARY:
+            continue
+        r = bench_decode(s, max(20, args.steps // 2), args.warmup) if isinstance(s, W.DecodeSpec) else \
+            bench_prefill(s, max(20, args.steps // 2), args.warmup)
+        results[s.name] = r
+        print(f"# {s.name}: {json.dumps(r)}", file=sys.stderr, flush=True)
+
+    torch.cuda.synchronize()
+    p = bench_prefill(PRIMARY, args.steps, args.warmup)
+    results[PRIMARY.name] = p
+    line = {
+        "metric": METRIC,
+        "value": round(p["tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(p["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": PRIMARY.name, "B": PRIMARY.B, "Hq": PRIMARY.Hq, "Hkv": PRIMARY.Hkv,
+                   "seq_len": PRIMARY.q_len, "D": PRIMARY.D, "causal": True,
+                   "global_batch": PRIMARY.B, "parallelism": "single GPU"},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(p["kernel_tflops"], 3),
+            "peak": PEAK_MFMA_16BIT_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(p["frac_of_peak"], 4),
+            "traffic": MEASURED_TRAFFIC_BYTES,
+            "kernel": "prefill_fwd_mfma<bf16, D=128, causal, 4 heads/workgroup>",
+            "kernel_ms_mean": round(p["kernel_ms_mean"], 5),
+        },
+        "workloads": results,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(PRIMARY)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
