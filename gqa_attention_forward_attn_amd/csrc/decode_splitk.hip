@@ -30,29 +30,16 @@ namespace {
 
 constexpr int kTile = 64;  // tokens per workgroup iteration (16 per wave)
 
-// Max over the 16 token lanes-quads of a wave (values are equal inside a quad).
-__device__ __forceinline__ float wave_max_over_quads(float x) {
-    x = fmaxf(x, dpp<kRowHalfMirror>(x));
-    x = fmaxf(x, dpp<kRowMirror>(x));
-    x = fmaxf(x, shfl_xor(x, 16));
-    x = fmaxf(x, xor32(x));
-    return x;
-}
-
-// Sum over the 16 lanes of a wave that share (lane & 3).
-__device__ __forceinline__ float wave_sum_same_quad_slot(float x) {
-    x += dpp<0x128>(x);  // row_ror:8
-    x += dpp<0x124>(x);  // row_ror:4
-    x += shfl_xor(x, 16);
-    x += xor32(x);
-    return x;
-}
+// Growth of a running max (log2 units) that triggers a rescale of acc and l;
+// acc and l always share the reference max, so the result is unchanged.
+constexpr float kRescaleLog2 = 8.f;
 
 template <class TAG, int D, int GH, bool PAGED>
-__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
-    constexpr int DQ = D / 4;      // dims per lane
-    constexpr int NCH = DQ / 8;    // 16-byte chunks per lane per row
-    constexpr int NW = DQ / 2;     // packed pairs per lane per row
+__global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
+    constexpr int DL = D / 16;        // dims per lane (16 lanes cover a token row)
+    constexpr int NWD = DL / 2;       // packed pairs per lane per row
+    constexpr int TPL = 4;            // tokens per lane per tile (stream r: t0 + 16w + r + 4j)
+    typedef uint32_t row_t __attribute__((ext_vector_type(NWD)));
 
     __shared__ float sm_acc[4][GH][D];
     __shared__ float sm_m[4][GH];
@@ -85,135 +72,167 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         return;
     }
 
-    const int dq = lane & 3;
-    const int tok_in_tile = 16 * wave + (lane >> 2);
+    const int c = lane & 15;   // dims [c*DL, c*DL + DL)
+    const int r = lane >> 4;   // token stream inside the wave
 
-    // q for the GH heads, this lane's dims, as packed pairs
-    uint32_t qw[GH][NW];
+    // q of the GH heads for this lane's dims, as packed pairs
+    row_t qw[GH];
 #pragma unroll
-    for (int j = 0; j < GH; ++j) {
-        const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + h0 + j) * D + dq * DQ;
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            const u32x4 t = ld_global_16(qp + c * 8);
-            qw[j][4 * c] = t[0]; qw[j][4 * c + 1] = t[1]; qw[j][4 * c + 2] = t[2]; qw[j][4 * c + 3] = t[3];
-        }
-    }
+    for (int j = 0; j < GH; ++j)
+        qw[j] = *reinterpret_cast<const row_t*>(static_cast<const uint16_t*>(a.q) +
+                                                ((size_t)b * a.Hq + h0 + j) * D + c * DL);
 
     const uint16_t* kbase = static_cast<const uint16_t*>(a.k);
     const uint16_t* vbase = static_cast<const uint16_t*>(a.v);
     const int* bt = PAGED ? a.block_table + (size_t)b * a.max_pages : nullptr;
     const int page_mask = (1 << a.page_shift) - 1;
-    auto row_offset = [&](int t) -> size_t {  // element offset of token t's row for head g
-        if (PAGED) {
-            const size_t page = (size_t)bt[t >> a.page_shift];
-            return ((page << a.page_shift) + (size_t)(t & page_mask)) * a.Hkv * D + (size_t)g * D;
+    const size_t head_off = PAGED ? (size_t)g * D : ((size_t)b * a.Hkv + g) * (size_t)a.max_kv_len * D;
+    const size_t tok_stride = PAGED ? (size_t)a.Hkv * D : (size_t)D;
+
+    auto tok_of = [&](int t0, int j) { return min(t0 + 16 * wave + r + 4 * j, hi - 1); };
+    // page ids of this lane's tokens in the tile at t0 (paged only)
+    auto fetch_pages = [&](int t0, int (&pg)[TPL]) {
+#pragma unroll
+        for (int j = 0; j < TPL; ++j) pg[j] = PAGED ? bt[tok_of(t0, j) >> a.page_shift] : 0;
+    };
+    auto row_index = [&](int t, int page) -> size_t {
+        if (PAGED) return (((size_t)page << a.page_shift) + (size_t)(t & page_mask)) * tok_stride + head_off;
+        return (size_t)t * tok_stride + head_off;
+    };
+    auto load = [&](int t0, const int (&pg)[TPL], row_t (&kr)[TPL], row_t (&vr)[TPL]) {
+#pragma unroll
+        for (int j = 0; j < TPL; ++j) {
+            const size_t off = row_index(tok_of(t0, j), pg[j]) + c * DL;
+            kr[j] = *reinterpret_cast<const row_t*>(kbase + off);
+            vr[j] = *reinterpret_cast<const row_t*>(vbase + off);
         }
-        return (((size_t)b * a.Hkv + g) * a.max_kv_len + t) * D;
     };
 
-    u32x4 kr[NCH], vr[NCH];
-    auto load = [&](int t0) {
-        const int t = min(t0 + tok_in_tile, hi - 1);
-        const size_t off = row_offset(t) + dq * DQ;
+    float m[GH], l[GH], acc[GH][DL];
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            kr[c] = ld_global_16(kbase + off + c * 8);
-            vr[c] = ld_global_16(vbase + off + c * 8);
-        }
-    };
-
-    float m[GH], l[GH], acc[GH][DQ];
+    for (int h = 0; h < GH; ++h) {
+        m[h] = -INFINITY;
+        l[h] = 0.f;
 #pragma unroll
-    for (int j = 0; j < GH; ++j) {
-        m[j] = -INFINITY;
-        l[j] = 0.f;
-#pragma unroll
-        for (int d = 0; d < DQ; ++d) acc[j][d] = 0.f;
+        for (int d = 0; d < DL; ++d) acc[h][d] = 0.f;
     }
 
-    load(lo);
-    for (int t0 = lo; t0 < hi; t0 += kTile) {
-        u32x4 kc[NCH], vc[NCH];
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) { kc[c] = kr[c]; vc[c] = vr[c]; }
-        if (t0 + kTile < hi) load(t0 + kTile);
+    // pipeline: page ids run one tile ahead of the K/V loads, which run one
+    // tile ahead of the arithmetic
+    int pg_next[TPL], pg_far[TPL];
+    row_t kc[TPL], vc[TPL], kn[TPL], vn[TPL];
+    fetch_pages(lo, pg_next);
+    load(lo, pg_next, kn, vn);
+    if (lo + kTile < hi) fetch_pages(lo + kTile, pg_far);
 
-        const bool valid = t0 + tok_in_tile < hi;
-        // scores of this lane's token for each head
-        float sc[GH];
+    for (int t0 = lo; t0 < hi; t0 += kTile) {
 #pragma unroll
-        for (int j = 0; j < GH; ++j) {
-            float x = 0.f;
+        for (int j = 0; j < TPL; ++j) { kc[j] = kn[j]; vc[j] = vn[j]; pg_next[j] = pg_far[j]; }
+        if (t0 + kTile < hi) load(t0 + kTile, pg_next, kn, vn);
+        if (t0 + 2 * kTile < hi) fetch_pages(t0 + 2 * kTile, pg_far);
+
+        // scores: this lane's 4 tokens x GH heads (reduced over the 16 lanes of the row)
+        float sc[TPL][GH];
 #pragma unroll
-            for (int c = 0; c < NCH; ++c)
+        for (int j = 0; j < TPL; ++j) {
+            const bool valid = t0 + 16 * wave + r + 4 * j < hi;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) x = dot2(TAG(), kc[c][e], qw[j][4 * c + e], x);
-            x += dpp<kQuadXor1>(x);
-            x += dpp<kQuadXor2>(x);
-            sc[j] = valid ? x : -INFINITY;
+            for (int h = 0; h < GH; ++h) {
+                float x = 0.f;
+#pragma unroll
+                for (int e = 0; e < NWD; ++e) x = dot2(TAG(), kc[j][e], qw[h][e], x);
+                x += dpp<kQuadXor1>(x);
+                x += dpp<kQuadXor2>(x);
+                x += dpp<kRowHalfMirror>(x);
+                x += dpp<kRowMirror>(x);
+                sc[j][h] = valid ? x : -INFINITY;
+            }
         }
-        float vf[DQ];
+        // wave-uniform running max per head; lazy rescale (see prefill)
+        float mt[GH];
+        bool grow = false;
 #pragma unroll
-        for (int c = 0; c < NCH; ++c)
+        for (int h = 0; h < GH; ++h) {
+            float x = fmaxf(fmaxf(sc[0][h], sc[1][h]), fmaxf(sc[2][h], sc[3][h]));
+            x = fmaxf(x, shfl_xor(x, 16));
+            x = fmaxf(x, xor32(x));
+            mt[h] = x * a.c;
+            grow |= mt[h] > m[h] + kRescaleLog2;
+        }
+        if (grow) {  // wave-uniform: mt and m are equal in every lane
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                vf[8 * c + 2 * e] = lo_to_f32(TAG(), vc[c][e]);
-                vf[8 * c + 2 * e + 1] = hi_to_f32(TAG(), vc[c][e]);
+            for (int h = 0; h < GH; ++h) {
+                const float m_new = fmaxf(m[h], mt[h]);
+                const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m[h] - m_new);
+                m[h] = m_new;
+                l[h] *= alpha;
+#pragma unroll
+                for (int d = 0; d < DL; ++d) acc[h][d] *= alpha;
+            }
+        }
+        // P.V on token pairs (j, j+1): dot2 of (p_j, p_j+1) with (v_j, v_j+1)
+#pragma unroll
+        for (int jp = 0; jp < TPL; jp += 2) {
+            uint32_t pp[GH];
+#pragma unroll
+            for (int h = 0; h < GH; ++h) {
+                const float mu = (m[h] == -INFINITY) ? 0.f : m[h];
+                const float p0 = fast_exp2(fmaf(sc[jp][h], a.c, -mu));
+                const float p1 = fast_exp2(fmaf(sc[jp + 1][h], a.c, -mu));
+                l[h] += p0 + p1;
+                pp[h] = pack2(TAG(), p0, p1);
             }
 #pragma unroll
-        for (int j = 0; j < GH; ++j) {
-            const float mx = wave_max_over_quads(sc[j]);
-            const float m_new = fmaxf(m[j], mx * a.c);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = fast_exp2(m[j] - m_use);
-            m[j] = m_new;
-            const float p = fast_exp2(fmaf(sc[j], a.c, -m_use));
-            l[j] = l[j] * alpha + p;
+            for (int e = 0; e < NWD; ++e) {
+                const uint32_t vlo = pack_lo(vc[jp][e], vc[jp + 1][e]);
+                const uint32_t vhi = pack_hi(vc[jp][e], vc[jp + 1][e]);
 #pragma unroll
-            for (int d = 0; d < DQ; ++d) acc[j][d] = fmaf(p, vf[d], acc[j][d] * alpha);
+                for (int h = 0; h < GH; ++h) {
+                    acc[h][2 * e] = dot2(TAG(), pp[h], vlo, acc[h][2 * e]);
+                    acc[h][2 * e + 1] = dot2(TAG(), pp[h], vhi, acc[h][2 * e + 1]);
+                }
+            }
         }
     }
 
-    // ---- merge the 16 token slots of each wave, then the 4 waves -------------
+    // ---- merge the 4 token streams of each wave (same m), then the 4 waves ----
 #pragma unroll
-    for (int j = 0; j < GH; ++j) {
-        // every lane of a quad holds the same l (same token); count one per quad
-        const float lq = (dq == 0) ? l[j] : 0.f;
-        float lw = lq;
-        lw += dpp<0x128>(lw);
-        lw += dpp<0x124>(lw);
-        lw += dpp<kQuadXor1>(lw);
-        lw += dpp<kQuadXor2>(lw);
+    for (int h = 0; h < GH; ++h) {
+        float lw = l[h];  // identical in the 16 lanes of a stream
         lw += shfl_xor(lw, 16);
         lw += xor32(lw);
 #pragma unroll
-        for (int d = 0; d < DQ; ++d) acc[j][d] = wave_sum_same_quad_slot(acc[j][d]);
-        if (lane < 4) {
+        for (int d = 0; d < DL; ++d) {
+            float x = acc[h][d];
+            x += shfl_xor(x, 16);
+            x += xor32(x);
+            acc[h][d] = x;
+        }
+        if (r == 0) {
 #pragma unroll
-            for (int d = 0; d < DQ; ++d) sm_acc[wave][j][dq * DQ + d] = acc[j][d];
+            for (int d = 0; d < DL; ++d) sm_acc[wave][h][c * DL + d] = acc[h][d];
         }
         if (lane == 0) {
-            sm_m[wave][j] = m[j];
-            sm_l[wave][j] = lw;
+            sm_m[wave][h] = m[h];
+            sm_l[wave][h] = lw;
         }
     }
     __syncthreads();
     for (int i = tid; i < GH * D; i += 256) {
-        const int j = i / D, d = i % D;
+        const int h = i / D, d = i % D;
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][j]);
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][h]);
         float L = 0.f, O = 0.f;
         if (M != -INFINITY) {
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                const float sc = fast_exp2(sm_m[w][j] - M);
-                L += sc * sm_l[w][j];
-                O += sc * sm_acc[w][j][d];
+                const float sc = fast_exp2(sm_m[w][h] - M);
+                L += sc * sm_l[w][h];
+                O += sc * sm_acc[w][h][d];
             }
         }
-        const size_t row = part_row0 + (size_t)j * a.n_splits;
+        const size_t row = part_row0 + (size_t)h * a.n_splits;
         a.part_o[row * D + d] = L > 0.f ? O / L : 0.f;
         if (d == 0) a.part_lse[row] = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
     }

@@ -112,6 +112,10 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
     return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
+// s_waitcnt vmcnt(0): every outstanding vector-memory load has returned.
+// (gfx9 encoding: vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].)
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ u32x4 ld_global_16(const void* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }

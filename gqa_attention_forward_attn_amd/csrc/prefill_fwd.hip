@@ -33,8 +33,11 @@ namespace gqa {
 
 namespace {
 
+// Growth of a row max (log2 units) that triggers a rescale of acc and l.
+constexpr float kRescaleLog2 = 8.f;
+
 template <class TAG, int D, bool CAUSAL, int NH>
-__global__ __launch_bounds__(256) void prefill_fwd_mfma(PrefillArgs a) {
+__global__ __launch_bounds__(256, 2) void prefill_fwd_mfma(PrefillArgs a) {
     constexpr int BN = 64;                 // keys per tile
     constexpr int WPH = 4 / NH;            // waves per head
     constexpr int POS = 32 * WPH;          // query positions per workgroup
@@ -93,6 +96,9 @@ __global__ __launch_bounds__(256) void prefill_fwd_mfma(PrefillArgs a) {
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds)
         qf[ds] = __builtin_bit_cast(vec8, ld_global_16(qp + (size_t)q_row * D + ds * 16 + half * 8));
+    // Q must be resident before the loop: otherwise the wait-count pass makes
+    // every use of Q inside the loop wait for the next tile's prefetch loads.
+    wait_vmcnt0();
 
     const size_t kv_head = ((size_t)b * a.Hkv + g) * (size_t)a.kv_len;
     const uint16_t* kp = static_cast<const uint16_t*>(a.k) + kv_head * D;
@@ -172,11 +178,14 @@ __global__ __launch_bounds__(256) void prefill_fwd_mfma(PrefillArgs a) {
             // S^T[key][query] for 64 keys (two 32-key halves)
             f32x16 s[2];
 #pragma unroll
-            for (int kh = 0; kh < 2; ++kh) {
+            for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[kh][r] = 0.f;
+            // the two 32-key halves are independent accumulation chains: interleave them
 #pragma unroll
-                for (int ds = 0; ds < DS; ++ds) {
+            for (int ds = 0; ds < DS; ++ds) {
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh) {
                     vec8 ka = *reinterpret_cast<const vec8*>(ks + (kh * 32 + l32) * KS + ds * 16 + half * 8);
                     s[kh] = mfma_32x32x16(ka, qf[ds], s[kh]);
                 }
@@ -199,13 +208,21 @@ __global__ __launch_bounds__(256) void prefill_fwd_mfma(PrefillArgs a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kh][r]);
             mx = fmaxf(mx, xor32(mx));
-            const float m_new = fmaxf(m, mx * a.c);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = fast_exp2(m - m_use);
-            m = m_new;
-            l *= alpha;
+            // Lazy rescale: the reference max m only moves when some row's max
+            // grew by more than kRescaleLog2 (log2 units).  acc and l always use
+            // the same m, so O = acc / l and LSE = m + log2 l are unchanged;
+            // weights stay below 2^kRescaleLog2.
+            const float m_tile = mx * a.c;
+            if (__builtin_amdgcn_ballot_w64(m_tile > m + kRescaleLog2)) {
+                const float m_new = fmaxf(m, m_tile);
+                // 0 when m = -inf; a row that has still seen no key keeps alpha = 1
+                const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m - m_new);
+                m = m_new;
+                l *= alpha;
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+                for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+            }
+            const float m_use = (m == -INFINITY) ? 0.f : m;
 
             uint32_t pk[2][8];
             float psum = 0.f;
@@ -308,6 +325,7 @@ __global__ __launch_bounds__(256) void prefill_fwd_f32(PrefillArgs a) {
         const f32x4 t = *reinterpret_cast<const f32x4*>(qp + (size_t)q_row * D + half * HD + j);
         qf[j] = t[0]; qf[j + 1] = t[1]; qf[j + 2] = t[2]; qf[j + 3] = t[3];
     }
+    wait_vmcnt0();
 
     const size_t kv_head = ((size_t)b * a.Hkv + g) * (size_t)a.kv_len;
     const float* kp = static_cast<const float*>(a.k) + kv_head * D;
@@ -381,13 +399,16 @@ __global__ __launch_bounds__(256) void prefill_fwd_f32(PrefillArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
             mx = fmaxf(mx, xor32(mx));
-            const float m_new = fmaxf(m, mx * a.c);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = fast_exp2(m - m_use);
-            m = m_new;
-            l *= alpha;
+            const float m_tile = mx * a.c;
+            if (__builtin_amdgcn_ballot_w64(m_tile > m + kRescaleLog2)) {
+                const float m_new = fmaxf(m, m_tile);
+                const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m - m_new);
+                m = m_new;
+                l *= alpha;
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+                for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+            }
+            const float m_use = (m == -INFINITY) ? 0.f : m;
             float p[16];
             float psum = 0.f;
 #pragma unroll
