@@ -27,6 +27,8 @@ struct PrefillArgs {
 
 // Validated arguments only.  D in {64, 128}; dtype one of kDtype*.
 hipError_t launch_prefill(PrefillArgs a, int D, bool causal, int dtype, hipStream_t stream);
+// Ping-pong schedule, 8 waves x 32 rows (bf16 / fp16 only).
+hipError_t launch_prefill_pp(PrefillArgs a, int D, bool causal, int dtype, hipStream_t stream);
 
 struct DecodeArgs {
     const void* q;            // [B, Hq, D]

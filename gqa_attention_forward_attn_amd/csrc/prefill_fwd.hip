@@ -486,6 +486,7 @@ hipError_t dispatch_d(PrefillArgs a, int D, bool causal, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_prefill(PrefillArgs a, int D, bool causal, int dtype, hipStream_t stream) {
+    if (dtype != kDtypeF32) return launch_prefill_pp(a, D, causal, dtype, stream);
     switch (dtype) {
     case kDtypeBF16: return dispatch_d<bf16_tag>(a, D, causal, stream);
     case kDtypeF16: return dispatch_d<f16_tag>(a, D, causal, stream);

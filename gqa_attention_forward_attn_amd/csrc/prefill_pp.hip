@@ -1,0 +1,410 @@
+// prefill_pp.hip - attention forward (prefill), ping-pong schedule.
+//
+// Method as in prefill_fwd.hip: FlashAttention forward with an online softmax
+// (causal_forward_kernel.py, `_flash_attention_forward_gqa_kernel`), the
+// bottom-right causal mask of the FlashInfer-style prefill page
+// (gpt-o3 / triton6fd1ef, `_gqa_prefill_kernel`) and the zero-fill of empty
+// rows of splitk_kernels.py (`_fwd_kernel_splitK`).
+//
+// Schedule.  On gfx950 the softmax of a 64-key x 32-query tile costs about as
+// many VALU cycles as the tile's 32 MFMAs, so matrix and vector work must
+// overlap.  A workgroup is 8 wave64s (two per SIMD), each owning 32 query
+// rows; the waves form two groups (waves 0-3 and 4-7, one of each per SIMD)
+// that run the same phase sequence one phase apart:
+//
+//     MFMA phase of tile t:  S(t) = K(t) Q^T, then acc += V(t-1) P(t-1)
+//     VALU phase of tile t:  mask, row max, lazy rescale, P(t) = exp2(...)
+//
+// separated by workgroup barriers, so while one wave of a SIMD issues MFMAs
+// the other runs its softmax.  K and V tiles (64 keys) are loaded straight
+// from global memory into four LDS stages (global_load_lds_dwordx4), two
+// tiles ahead; V stays row-major and is read with ds_read_b64_tr_b16 into
+// the P.V MFMA's A operand.
+#include "gqa_device.hpp"
+#include "gqa_kernels.hpp"
+
+namespace gqa {
+
+namespace {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr float kRescaleLog2p = 8.f;
+
+#ifndef PP_AHEAD
+#define PP_AHEAD 8
+#endif
+
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x8;
+constexpr int kSchedDsRead = 0x100;
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without a memory fence (outstanding direct-to-LDS loads
+// of later tiles stay in flight); the empty asm statements keep the compiler
+// from moving LDS accesses across it.
+__device__ __forceinline__ void barrier_no_fence() {
+    __asm__ __volatile__("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ __volatile__("" ::: "memory");
+}
+
+// 16 bytes per lane from global memory into LDS (lane i -> lds_base + 16 i).
+// Inline asm so the compiler's wait-count pass does not make every later LDS
+// read wait for it; completion is awaited explicitly (vmcnt + barrier).
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+    __asm__ __volatile__("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                         :
+                         : "v"(gptr), "s"(lds_base)
+                         : "m0");
+}
+
+__device__ __forceinline__ u32x2 lds_read_tr(const lds_char* p) {
+    i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
+    return __builtin_bit_cast(u32x2, v);
+}
+
+// LDS tile layout: rows of D*2 bytes, 16-byte chunk c of row r stored at chunk
+// position c ^ swz<D>(r).  LDS has 64 banks of 4 bytes: a 16-byte read is
+// served 16 lanes at a time and an 8-byte read 32 lanes at a time, so a read
+// is conflict-free when those lanes cover 16 distinct 16-byte bank groups.
+// K operand reads: 16 lanes = 16 consecutive rows at one chunk; transposed V
+// reads: 32 lanes = 4 consecutive rows x 4 adjacent chunks.  D = 128: one row
+// spans all 64 banks, group = position, and swz is a bijection on r % 16 whose
+// value >> 2 differs across any 4 aligned rows.  D = 64: two rows per bank
+// row, group = 8 (r % 2) + position, and swz is a bijection on (r >> 1) % 8
+// differing in bit 2 between rows r and r + 2.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+    if (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+    return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
+
+template <class TAG, int D, bool CAUSAL, int NH>
+__global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
+    constexpr int NW = 8;                  // waves per workgroup
+    constexpr int BN = 64;                 // keys per tile
+    constexpr int WPH = NW / NH;           // waves per head
+    constexpr int POS = 32 * WPH;          // query positions per workgroup
+    constexpr int CPR = D / 8;             // 16-byte chunks per row
+    constexpr int ROWB = D * 2;
+    constexpr int TILEB = BN * ROWB;
+    constexpr int STAGEB = 2 * TILEB;
+    constexpr int NST = 4;
+    constexpr int DS = D / 16;
+    constexpr int DT = D / 32;
+    constexpr int LPW = CPR / NW;          // direct-load instructions per wave per tile, each of K and V
+    static_assert(LPW >= 1, "tile too small for the workgroup");
+    typedef typename TAG::vec8 vec8;
+
+    __shared__ __attribute__((aligned(1024))) char smem_raw[NST * STAGEB];
+    lds_char* smem = (lds_char*)smem_raw;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int grp = wave >> 2;             // ping-pong group: 0 leads, 1 trails by one phase
+    const int half = lane >> 5;
+    const int l32 = lane & 31;
+
+    // ---- work item ----------------------------------------------------------
+    int pt = blockIdx.x / a.n_rest;
+    int rest = blockIdx.x - pt * a.n_rest;
+    if (CAUSAL) pt = a.n_pos_tiles - 1 - pt;  // longest rows first
+    const int hgroups = a.group / NH;
+    const int hg = rest % hgroups;
+    rest /= hgroups;
+    const int g = rest % a.Hkv;
+    const int b = rest / a.Hkv;
+    const int h = g * a.group + hg * NH + wave / WPH;
+    const int wg_pos0 = pt * POS;
+    const int pos0 = wg_pos0 + (wave % WPH) * 32;
+    const int my_q = pos0 + l32;
+
+    int wg_kv_end = a.kv_len, wave_full_end = a.kv_len;
+    if (CAUSAL) {
+        const int wg_last = min(wg_pos0 + POS, a.q_len) - 1;
+        wg_kv_end = max(0, min(a.kv_len, wg_last + a.delta + 1));
+        wave_full_end = max(0, min(a.kv_len, pos0 + a.delta + 1));
+    }
+    const int n_tiles = (wg_kv_end + BN - 1) / BN;
+    const int n_full = min(wave_full_end / BN, n_tiles);
+    const int lim = CAUSAL ? min(my_q + a.delta + 1, a.kv_len) : a.kv_len;  // keys < lim are visible
+
+    // ---- Q (B operand of S^T = K Q^T) ---------------------------------------
+    const size_t q_head = ((size_t)b * a.Hq + h) * (size_t)a.q_len;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + q_head * D;
+    vec8 qf[DS];
+    {
+        const int row = min(my_q, a.q_len - 1);
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds)
+            qf[ds] = __builtin_bit_cast(vec8, ld_global_16(qp + (size_t)row * D + ds * 16 + half * 8));
+    }
+    wait_vmcnt<0>();
+
+    // ---- direct global -> LDS tile loads --------------------------------------
+    const size_t kv_head = ((size_t)b * a.Hkv + g) * (size_t)a.kv_len;
+    const char* kg = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.k) + kv_head * D);
+    const char* vg = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.v) + kv_head * D);
+    const int last_key = a.kv_len - 1;
+    int ld_row[LPW], ld_col[LPW];
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+        const int p = (wave * LPW + j) * 64 + lane;  // chunk position in the tile
+        const int row = p / CPR, pc = p % CPR;
+        ld_row[j] = row;
+        ld_col[j] = (pc ^ swz<D>(row)) * 16;
+    }
+    auto issue_tile = [&](int t) {
+        const int t0 = t * BN;
+        lds_char* st = smem + (t % NST) * STAGEB;
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) {
+            const size_t off = (size_t)min(t0 + ld_row[j], last_key) * ROWB + ld_col[j];
+            const uint32_t dst = (uint32_t)(uintptr_t)(st + (wave * LPW + j) * 1024);
+            dma16(kg + off, __builtin_amdgcn_readfirstlane(dst));
+            dma16(vg + off, __builtin_amdgcn_readfirstlane(dst + TILEB));
+        }
+    };
+
+    // ---- per-lane LDS read offsets ---------------------------------------------
+    int k_off[DS];  // K operand: row l32 (+32 kh), chunk 2 ds + half
+    {
+        const int sw = swz<D>(l32);
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) k_off[ds] = l32 * ROWB + (((2 * ds + half) ^ sw) * 16);
+    }
+    // V operand through transposed reads: in each 16-lane group, source lane s
+    // reads row kbase + s/4, dims d0 + 4 (s%4) .. +3 with d0 = 32 dt + 16 ((lane/16)&1)
+    // and kbase = 16 k16 + 8 rd + 4 half; it returns 4 consecutive keys of one dim.
+    int v_off[2][DT];  // [rd][dt]: the two 4-key halves of each 16-key step
+    {
+        const int s = lane & 15;
+        const int g1 = (lane >> 4) & 1;
+#pragma unroll
+        for (int rd = 0; rd < 2; ++rd) {
+            const int rsub = 8 * rd + 4 * half + (s >> 2);  // row inside the 16-row block
+            const int sw = swz<D>(rsub);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const int c = 4 * dt + 2 * g1 + ((s & 3) >> 1);
+                v_off[rd][dt] = rsub * ROWB + ((c ^ sw) * 16) + (s & 1) * 8;
+            }
+        }
+    }
+
+    // ---- state -------------------------------------------------------------------
+    float m = -INFINITY;
+    float l = 0.f;            // this lane's share of the row sum (its half of the keys)
+    f32x16 acc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+    f32x16 s[2];               // S^T of the current tile, two 32-key halves
+    uint32_t pk[16];           // packed P of the previous tile (pairs of keys)
+
+    // MFMA phase pieces: the scores of tile t, and the P.V of tile t-1
+    auto scores = [&](int t) {
+        const lds_char* sk = smem + (t % NST) * STAGEB;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kh][r] = 0.f;
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) {
+                const vec8 ka = *reinterpret_cast<const __attribute__((address_space(3))) vec8*>(
+                    sk + kh * 32 * ROWB + k_off[ds]);
+                s[kh] = mfma_32x32x16(ka, qf[ds], s[kh]);
+            }
+    };
+    auto pv = [&](int t) {  // P.V of tile t - 1
+        const lds_char* sv = smem + ((t - 1) % NST) * STAGEB + TILEB;
+#pragma unroll
+        for (int k16 = 0; k16 < 4; ++k16) {
+            const u32x4 pw = {pk[4 * k16], pk[4 * k16 + 1], pk[4 * k16 + 2], pk[4 * k16 + 3]};
+            const vec8 pb = __builtin_bit_cast(vec8, pw);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const u32x2 lo = lds_read_tr(sv + 16 * k16 * ROWB + v_off[0][dt]);
+                const u32x2 hi = lds_read_tr(sv + 16 * k16 * ROWB + v_off[1][dt]);
+                const u32x4 vw = {lo[0], lo[1], hi[0], hi[1]};
+                acc[dt] = mfma_32x32x16(__builtin_bit_cast(vec8, vw), pb, acc[dt]);
+            }
+        }
+    };
+    // Interior MFMA phase (0 < t < n_tiles): one basic block, operand reads
+    // kept about eight MFMAs ahead of their use (LDS latency is several
+    // MFMA issue slots).
+    auto mfma_phase = [&](int t) {
+        scores(t);
+        pv(t);
+        constexpr int NS = 2 * DS;   // score MFMAs (one K read each)
+        constexpr int NP = 4 * DT;   // P.V MFMAs (two transposed reads each)
+        constexpr int AHEAD = PP_AHEAD;
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, AHEAD, 0);
+#pragma unroll
+        for (int i = 0; i < NS - AHEAD; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < AHEAD; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < NP - AHEAD / 2; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            if (i < NP - AHEAD) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        }
+    };
+    auto scores_only = [&](int t) {
+        scores(t);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * DS; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            if (i + 8 < 2 * DS) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+    };
+    auto pv_only = [&](int t) {
+        pv(t);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
+#pragma unroll
+        for (int i = 0; i < 4 * DT; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            if (i + 4 < 4 * DT) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        }
+    };
+
+    // VALU phase of tile t: mask, row max, lazy rescale, weights
+    auto valu_phase = [&](int t) {
+        if (t >= n_full) {  // diagonal / tail tile
+            const int k0 = t * BN;
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + kh * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                    s[kh][r] = key < lim ? s[kh][r] : -INFINITY;
+                }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kh][r]);
+        mx = fmaxf(mx, xor32(mx));
+        const float mt = mx * a.c;
+        // lazy rescale: the reference max moves only when a row max grew by more
+        // than 2^kRescaleLog2p; acc and l share it, so O and the LSE are unchanged
+        if (__builtin_amdgcn_ballot_w64(mt > m + kRescaleLog2p)) {
+            const float m_new = fmaxf(m, mt);
+            const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m - m_new);
+            m = m_new;
+            l *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+        }
+        const float mu = m == -INFINITY ? 0.f : m;
+        float ls = 0.f;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const float p0 = fast_exp2(fmaf(s[kh][r], a.c, -mu));
+                const float p1 = fast_exp2(fmaf(s[kh][r + 1], a.c, -mu));
+                pk[kh * 8 + (r >> 1)] = pack2(TAG(), p0, p1);
+                ls += p0 + p1;  // row sum of the unrounded weights
+            }
+        l += ls;
+    };
+
+    // ---- phase loop ----------------------------------------------------------------
+    // Phase p: group 0 runs the MFMA phase of tile p/2 when p is even and the
+    // VALU phase of tile p/2 when p is odd; group 1 runs the same one phase
+    // later.  Every wave passes one barrier per phase.
+    if (n_tiles > 0) {
+        issue_tile(0);
+        if (n_tiles > 1) issue_tile(1);
+        const int n_phases = 2 * n_tiles + 2;
+        for (int p = 0; p < n_phases; ++p) {
+            if ((p & 1) == 0) {  // tile p/2 is read from this phase on
+                const int t = p >> 1;
+                if (t < n_tiles) {
+                    if (t + 1 < n_tiles) wait_vmcnt<2 * LPW>(); else wait_vmcnt<0>();
+                }
+            }
+            barrier_no_fence();
+            if ((p & 1) == 0 && (p >> 1) + 2 < n_tiles) issue_tile((p >> 1) + 2);
+            const int q = p - grp;
+            if (q < 0 || q > 2 * n_tiles) continue;
+            const int t = q >> 1;
+            if (q & 1) valu_phase(t);
+            else if (t == 0) scores_only(0);
+            else if (t == n_tiles) pv_only(t);
+            else mfma_phase(t);
+        }
+    }
+
+    // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----------------------------
+    const float l_tot = l + xor32(l);
+    if (my_q < a.q_len) {
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        uint16_t* op = static_cast<uint16_t*>(a.o) + (q_head + my_q) * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d0 = dt * 32 + 8 * r4 + 4 * half;
+                const u32x2 w = {pack2(TAG(), acc[dt][4 * r4] * inv, acc[dt][4 * r4 + 1] * inv),
+                                 pack2(TAG(), acc[dt][4 * r4 + 2] * inv, acc[dt][4 * r4 + 3] * inv)};
+                *reinterpret_cast<u32x2*>(op + d0) = w;
+            }
+        if (half == 0) a.lse[q_head + my_q] = l_tot > 0.f ? (m + fast_log2(l_tot)) * kLn2 : -INFINITY;
+    }
+}
+
+template <class TAG, int D, bool CAUSAL, int NH>
+hipError_t launch_pp(PrefillArgs a, hipStream_t stream) {
+    constexpr int POS = 256 / NH;
+    a.n_pos_tiles = (a.q_len + POS - 1) / POS;
+    a.n_rest = a.B * a.Hkv * (a.group / NH);
+    const long long blocks = (long long)a.n_pos_tiles * a.n_rest;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((prefill_fwd_pp<TAG, D, CAUSAL, NH>), dim3((unsigned)blocks), dim3(512), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <class TAG, int D, bool CAUSAL>
+hipError_t dispatch_nh(PrefillArgs a, hipStream_t stream) {
+    if (a.group % 8 == 0) return launch_pp<TAG, D, CAUSAL, 8>(a, stream);
+    if (a.group % 4 == 0) return launch_pp<TAG, D, CAUSAL, 4>(a, stream);
+    if (a.group % 2 == 0) return launch_pp<TAG, D, CAUSAL, 2>(a, stream);
+    return launch_pp<TAG, D, CAUSAL, 1>(a, stream);
+}
+
+template <class TAG>
+hipError_t dispatch_d(PrefillArgs a, int D, bool causal, hipStream_t stream) {
+    if (D == 64) return causal ? dispatch_nh<TAG, 64, true>(a, stream) : dispatch_nh<TAG, 64, false>(a, stream);
+    return causal ? dispatch_nh<TAG, 128, true>(a, stream) : dispatch_nh<TAG, 128, false>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_prefill_pp(PrefillArgs a, int D, bool causal, int dtype, hipStream_t stream) {
+    if (dtype == kDtypeBF16) return dispatch_d<bf16_tag>(a, D, causal, stream);
+    return dispatch_d<f16_tag>(a, D, causal, stream);
+}
+
+}  // namespace gqa
