@@ -18,6 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJ_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libgqa_attn.so")
 SOURCES = ["prefill_fwd.hip", "prefill_pp.hip", "decode_splitk.hip", "api.cpp"]
+# per-source compiler options (none at present)
+EXTRA_FLAGS: dict = {}
 
 
 def hipcc() -> str:
@@ -42,7 +44,7 @@ def compile_flags(save_temps: bool = False) -> list:
 
 def _compile(src: str, save_temps: bool) -> str:
     obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + compile_flags(save_temps) + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + compile_flags(save_temps) + EXTRA_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True, cwd=OBJ_DIR)
     # the host pass does not know the gfx950 feature name; that warning is expected
     noise = "is not a recognized feature for this target"

@@ -86,7 +86,7 @@ gqa_status_t attn_decode_splitk(const void* q, const void* k, const void* v, voi
         if ((long long)max_pages_per_seq * page_size < (long long)max_kv_len) return GQA_ERR_INVALID_ARG;
         while ((1 << page_shift) < page_size) ++page_shift;
     }
-    if (!supported_head_dim(D) || dtype == GQA_F32 || Hq / Hkv > 8) return GQA_ERR_UNSUPPORTED;
+    if (!supported_head_dim(D) || dtype == GQA_F32) return GQA_ERR_UNSUPPORTED;
     if (B == 0) return GQA_OK;
     if (!q || !k || !v || !o || !lse || !seq_lens) return GQA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return GQA_ERR_INVALID_ARG;

@@ -2,25 +2,33 @@
 //
 // Method: splitk_kernels.py (xformers), `_fwd_kernel_splitK` and
 // `_splitK_reduce`.  Each sequence's keys are cut into n_splits chunks; every
-// chunk runs the online softmax over its keys and writes a partial output
-// O_s = acc / l (0 when the chunk is empty) and its natural-base LSE
-// (-inf when empty).  The combine kernel merges the chunks per (b, h):
-// M = max_s LSE_s, w_s = exp(LSE_s - M), O = sum w_s O_s / sum w_s,
-// LSE = M + log(sum w_s); all chunks empty gives (0, -inf).  Keys of a paged
-// cache are found through the per-sequence block table, page
-// block_table[b, t / page_size], row t % page_size (the PAGE_SIZE branch of
-// `_fwd_kernel_splitK`).
+// non-empty chunk runs the online softmax over its keys and writes a partial
+// output O_s = acc / l and its natural-base LSE.  The combine kernel merges the
+// chunks per (b, h): M = max_s LSE_s, w_s = exp(LSE_s - M),
+// O = sum w_s O_s / sum w_s, LSE = M + log(sum w_s); a sequence with no keys
+// gives (0, -inf).  Keys of a paged cache are found through the per-sequence
+// block table, page block_table[b, t / page_size], row t % page_size (the
+// PAGE_SIZE branch of `_fwd_kernel_splitK`).
 //
-// gfx950 mapping.  Decode reads every K/V byte once and does ~4 flop per
-// byte, so it is bound by HBM and runs on the vector ALUs: no MFMA padding of
-// the 4-row query block.  A workgroup (4 wave64s) owns one (sequence, K/V head,
-// chunk) and every query head of the group (up to 4 per workgroup).  Each wave
-// takes 16 tokens of every 64-token tile; a token row is read by 4 lanes with
-// 16-byte loads, so a wave's load instruction covers 16 rows x 64 contiguous
-// bytes.  q.k uses packed 2-wide dot products (v_dot2_f32_bf16 / _f16) and a
-// quad reduction (DPP), the softmax state is per wave, and the waves are merged
-// through LDS at the end of the chunk.  The next tile's loads are issued
-// before the current tile is consumed.
+// gfx950 mapping.  Decode reads every K/V byte once, so it is bound by HBM;
+// the arithmetic still goes to the matrix cores so that the vector ALUs stay
+// nearly idle.  A workgroup owns one (sequence, K/V head, chunk) and up to 16
+// query heads of the group, which are the 16 columns of the MFMA tiles (heads
+// beyond the group are zero columns).  Each wave streams its own 16-token
+// slices of the chunk (wave w takes slices w, w + NW, ...):
+//
+//   K, V slice (16 rows)  --global_load_lds_dwordx4-->  per-wave LDS ring of NST stages
+//   S^T[16 tok x 16 heads] = K q^T        4 x v_mfma_f32_16x16x32 (D = 128)
+//   online softmax on S^T (4 values per lane, no cross-lane work unless the
+//                          running max grows by more than 2^8)
+//   O[16 heads x D] += P V                8 x v_mfma_f32_16x16x16 with V read
+//                                         transposed (ds_read_b64_tr_b16)
+//
+// The S^T result layout (lane: head l%16, tokens 4(l/16)..+3) is exactly the
+// A-operand layout of the P.V MFMA, so P never leaves its registers.  Loads run
+// NST-1 slices ahead of the arithmetic and no barrier is taken in the loop:
+// every wave waits only for its own loads.  The NW per-wave partial results are
+// merged through LDS at the end of the chunk.
 #include "gqa_device.hpp"
 #include "gqa_kernels.hpp"
 
@@ -28,238 +36,375 @@ namespace gqa {
 
 namespace {
 
-constexpr int kTile = 64;  // tokens per workgroup iteration (16 per wave)
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+typedef const __attribute__((address_space(4))) int const_int;
 
-// Growth of a running max (log2 units) that triggers a rescale of acc and l;
-// acc and l always share the reference max, so the result is unchanged.
+constexpr int kSlice = 16;         // tokens per slice (MFMA rows)
 constexpr float kRescaleLog2 = 8.f;
 
-template <class TAG, int D, int GH, bool PAGED>
-__global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
-    constexpr int DL = D / 16;        // dims per lane (16 lanes cover a token row)
-    constexpr int NWD = DL / 2;       // packed pairs per lane per row
-    constexpr int TPL = 4;            // tokens per lane per tile (stream r: t0 + 16w + r + 4j)
-    typedef uint32_t row_t __attribute__((ext_vector_type(NWD)));
+// K/V addressing of the split kernel
+enum { kDense = 0, kPaged = 1, kPagedSmall = 2 };
 
-    __shared__ float sm_acc[4][GH][D];
-    __shared__ float sm_m[4][GH];
-    __shared__ float sm_l[4][GH];
+#ifndef DEC_NW
+#define DEC_NW 4
+#endif
+#ifndef DEC_NST
+#define DEC_NST 4
+#endif
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n_hb = a.group / GH;
-    int id = blockIdx.x;
-    const int s = id % a.n_splits;
-    id /= a.n_splits;
-    const int hb = id % n_hb;
-    id /= n_hb;
-    const int g = id % a.Hkv;
-    const int b = id / a.Hkv;
-    const int h0 = g * a.group + hb * GH;
+// Chunk length of the split-K partition (a multiple of 64 tokens); both kernels
+// derive the chunk bounds from it.
+__device__ __forceinline__ int chunk_tokens(int len, int n_splits) {
+    const int per = (len + n_splits - 1) / n_splits;
+    return (per + 63) / 64 * 64;
+}
 
-    const int len = a.seq_lens[b];
-    const int per = (len + a.n_splits - 1) / a.n_splits;
-    const int chunk = (per + kTile - 1) / kTile * kTile;
-    const int lo = s * chunk;
-    const int hi = min(len, lo + chunk);
+// 16 bytes per lane from global memory into LDS (lane i -> lds + 16 i).  The
+// compiler does not see the load, so completion is awaited with explicit
+// vmcnt waits; the memory clobber keeps LDS reads of the stage it overwrites
+// on their side of it.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
+    __asm__ __volatile__("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                         :
+                         : "v"(gptr), "s"(lds)
+                         : "m0", "memory");
+}
+// Same, from a wave-uniform base address plus a 32-bit per-lane byte offset.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+    __asm__ __volatile__("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                         :
+                         : "v"(voff), "s"(sbase), "s"(lds)
+                         : "m0", "memory");
+}
 
-    const size_t part_row0 = ((size_t)b * a.Hq + h0) * a.n_splits + s;  // head h0, split s
-    if (lo >= hi) {  // empty chunk: (0, -inf)
-        for (int i = tid; i < GH * D; i += 256) {
-            const int j = i / D, d = i % D;
-            a.part_o[(part_row0 + (size_t)j * a.n_splits) * D + d] = 0.f;
-        }
-        if (tid < GH) a.part_lse[part_row0 + (size_t)tid * a.n_splits] = -INFINITY;
-        return;
-    }
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+    __asm__ __volatile__("" ::: "memory");
+}
 
-    const int c = lane & 15;   // dims [c*DL, c*DL + DL)
-    const int r = lane >> 4;   // token stream inside the wave
-
-    // q of the GH heads for this lane's dims, as packed pairs
-    row_t qw[GH];
-#pragma unroll
-    for (int j = 0; j < GH; ++j)
-        qw[j] = *reinterpret_cast<const row_t*>(static_cast<const uint16_t*>(a.q) +
-                                                ((size_t)b * a.Hq + h0 + j) * D + c * DL);
-
-    const uint16_t* kbase = static_cast<const uint16_t*>(a.k);
-    const uint16_t* vbase = static_cast<const uint16_t*>(a.v);
-    const int* bt = PAGED ? a.block_table + (size_t)b * a.max_pages : nullptr;
-    const int page_mask = (1 << a.page_shift) - 1;
-    const size_t head_off = PAGED ? (size_t)g * D : ((size_t)b * a.Hkv + g) * (size_t)a.max_kv_len * D;
-    const size_t tok_stride = PAGED ? (size_t)a.Hkv * D : (size_t)D;
-
-    auto tok_of = [&](int t0, int j) { return min(t0 + 16 * wave + r + 4 * j, hi - 1); };
-    // page ids of this lane's tokens in the tile at t0 (paged only)
-    auto fetch_pages = [&](int t0, int (&pg)[TPL]) {
-#pragma unroll
-        for (int j = 0; j < TPL; ++j) pg[j] = PAGED ? bt[tok_of(t0, j) >> a.page_shift] : 0;
-    };
-    auto row_index = [&](int t, int page) -> size_t {
-        if (PAGED) return (((size_t)page << a.page_shift) + (size_t)(t & page_mask)) * tok_stride + head_off;
-        return (size_t)t * tok_stride + head_off;
-    };
-    auto load = [&](int t0, const int (&pg)[TPL], row_t (&kr)[TPL], row_t (&vr)[TPL]) {
-#pragma unroll
-        for (int j = 0; j < TPL; ++j) {
-            const size_t off = row_index(tok_of(t0, j), pg[j]) + c * DL;
-            kr[j] = *reinterpret_cast<const row_t*>(kbase + off);
-            vr[j] = *reinterpret_cast<const row_t*>(vbase + off);
-        }
-    };
-
-    float m[GH], l[GH], acc[GH][DL];
-#pragma unroll
-    for (int h = 0; h < GH; ++h) {
-        m[h] = -INFINITY;
-        l[h] = 0.f;
-#pragma unroll
-        for (int d = 0; d < DL; ++d) acc[h][d] = 0.f;
-    }
-
-    // pipeline: page ids run one tile ahead of the K/V loads, which run one
-    // tile ahead of the arithmetic
-    int pg_next[TPL], pg_far[TPL];
-    row_t kc[TPL], vc[TPL], kn[TPL], vn[TPL];
-    fetch_pages(lo, pg_next);
-    load(lo, pg_next, kn, vn);
-    if (lo + kTile < hi) fetch_pages(lo + kTile, pg_far);
-
-    for (int t0 = lo; t0 < hi; t0 += kTile) {
-#pragma unroll
-        for (int j = 0; j < TPL; ++j) { kc[j] = kn[j]; vc[j] = vn[j]; pg_next[j] = pg_far[j]; }
-        if (t0 + kTile < hi) load(t0 + kTile, pg_next, kn, vn);
-        if (t0 + 2 * kTile < hi) fetch_pages(t0 + 2 * kTile, pg_far);
-
-        // scores: this lane's 4 tokens x GH heads (reduced over the 16 lanes of the row)
-        float sc[TPL][GH];
-#pragma unroll
-        for (int j = 0; j < TPL; ++j) {
-            const bool valid = t0 + 16 * wave + r + 4 * j < hi;
-#pragma unroll
-            for (int h = 0; h < GH; ++h) {
-                float x = 0.f;
-#pragma unroll
-                for (int e = 0; e < NWD; ++e) x = dot2(TAG(), kc[j][e], qw[h][e], x);
-                x += dpp<kQuadXor1>(x);
-                x += dpp<kQuadXor2>(x);
-                x += dpp<kRowHalfMirror>(x);
-                x += dpp<kRowMirror>(x);
-                sc[j][h] = valid ? x : -INFINITY;
-            }
-        }
-        // wave-uniform running max per head; lazy rescale (see prefill)
-        float mt[GH];
-        bool grow = false;
-#pragma unroll
-        for (int h = 0; h < GH; ++h) {
-            float x = fmaxf(fmaxf(sc[0][h], sc[1][h]), fmaxf(sc[2][h], sc[3][h]));
-            x = fmaxf(x, shfl_xor(x, 16));
-            x = fmaxf(x, xor32(x));
-            mt[h] = x * a.c;
-            grow |= mt[h] > m[h] + kRescaleLog2;
-        }
-        if (grow) {  // wave-uniform: mt and m are equal in every lane
-#pragma unroll
-            for (int h = 0; h < GH; ++h) {
-                const float m_new = fmaxf(m[h], mt[h]);
-                const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m[h] - m_new);
-                m[h] = m_new;
-                l[h] *= alpha;
-#pragma unroll
-                for (int d = 0; d < DL; ++d) acc[h][d] *= alpha;
-            }
-        }
-        // P.V on token pairs (j, j+1): dot2 of (p_j, p_j+1) with (v_j, v_j+1)
-#pragma unroll
-        for (int jp = 0; jp < TPL; jp += 2) {
-            uint32_t pp[GH];
-#pragma unroll
-            for (int h = 0; h < GH; ++h) {
-                const float mu = (m[h] == -INFINITY) ? 0.f : m[h];
-                const float p0 = fast_exp2(fmaf(sc[jp][h], a.c, -mu));
-                const float p1 = fast_exp2(fmaf(sc[jp + 1][h], a.c, -mu));
-                l[h] += p0 + p1;
-                pp[h] = pack2(TAG(), p0, p1);
-            }
-#pragma unroll
-            for (int e = 0; e < NWD; ++e) {
-                const uint32_t vlo = pack_lo(vc[jp][e], vc[jp + 1][e]);
-                const uint32_t vhi = pack_hi(vc[jp][e], vc[jp + 1][e]);
-#pragma unroll
-                for (int h = 0; h < GH; ++h) {
-                    acc[h][2 * e] = dot2(TAG(), pp[h], vlo, acc[h][2 * e]);
-                    acc[h][2 * e + 1] = dot2(TAG(), pp[h], vhi, acc[h][2 * e + 1]);
-                }
-            }
-        }
-    }
-
-    // ---- merge the 4 token streams of each wave (same m), then the 4 waves ----
-#pragma unroll
-    for (int h = 0; h < GH; ++h) {
-        float lw = l[h];  // identical in the 16 lanes of a stream
-        lw += shfl_xor(lw, 16);
-        lw += xor32(lw);
-#pragma unroll
-        for (int d = 0; d < DL; ++d) {
-            float x = acc[h][d];
-            x += shfl_xor(x, 16);
-            x += xor32(x);
-            acc[h][d] = x;
-        }
-        if (r == 0) {
-#pragma unroll
-            for (int d = 0; d < DL; ++d) sm_acc[wave][h][c * DL + d] = acc[h][d];
-        }
-        if (lane == 0) {
-            sm_m[wave][h] = m[h];
-            sm_l[wave][h] = lw;
-        }
-    }
-    __syncthreads();
-    for (int i = tid; i < GH * D; i += 256) {
-        const int h = i / D, d = i % D;
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][h]);
-        float L = 0.f, O = 0.f;
-        if (M != -INFINITY) {
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const float sc = fast_exp2(sm_m[w][h] - M);
-                L += sc * sm_l[w][h];
-                O += sc * sm_acc[w][h][d];
-            }
-        }
-        const size_t row = part_row0 + (size_t)h * a.n_splits;
-        a.part_o[row * D + d] = L > 0.f ? O / L : 0.f;
-        if (d == 0) a.part_lse[row] = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
+// Wait until at most n * PER direct loads are outstanding (n < 8).
+template <int PER>
+__device__ __forceinline__ void wait_slices(int n) {
+    switch (n) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<1 * PER>(); break;
+    case 2: wait_vm<2 * PER>(); break;
+    case 3: wait_vm<3 * PER>(); break;
+    case 4: wait_vm<(4 * PER < 64 ? 4 * PER : 63)>(); break;
+    case 5: wait_vm<(5 * PER < 64 ? 5 * PER : 63)>(); break;
+    case 6: wait_vm<(6 * PER < 64 ? 6 * PER : 63)>(); break;
+    default: wait_vm<(7 * PER < 64 ? 7 * PER : 63)>(); break;
     }
 }
 
-// One wave per (b, h): merge the n_splits partial results.
+__device__ __forceinline__ u32x4 lds16(const lds_char* p) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(p);
+}
+__device__ __forceinline__ u32x2 lds_tr(const lds_char* p) {
+    i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
+    return __builtin_bit_cast(u32x2, v);
+}
+
+// D[16x16] += A[16x32] B[32x16]; lane l holds row/column l % 16 and k-slots
+// 8(l/16)..+7; result lane l: column l % 16, rows 4(l/16)..+3.
+__device__ __forceinline__ f32x4 mfma16x32(bf16_tag, u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                    c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x32(f16_tag, u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
+                                                   c, 0, 0, 0);
+}
+// D[16x16] += A[16x16] B[16x16]; k-slots 4(l/16)..+3, same result layout.
+__device__ __forceinline__ f32x4 mfma16x16(bf16_tag, u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a), __builtin_bit_cast(i16x4, b),
+                                                      c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16(f16_tag, u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b),
+                                                  c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float lane_value(float x, int src_lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src_lane << 2, __builtin_bit_cast(int, x)));
+}
+
+// LDS slice layout: 16 rows of 2D bytes; 16-byte chunk c of row r is stored at
+// chunk position c ^ swz<D>(r).  LDS has 64 banks of 4 bytes; a 16-byte read is
+// served 16 lanes at a time, an 8-byte read 32 lanes at a time, and a read is
+// conflict-free when those lanes hit distinct 16-byte bank groups.  K / q
+// operand reads: 16 lanes = rows 0..15 at one chunk.  Transposed V reads: 32
+// lanes = 8 consecutive rows x chunks (2n, 2n+1).  D = 128 (a row spans all 64
+// banks): swz is a bijection on r % 16 that is even on rows 0-7 and odd on rows
+// 8-15.  D = 64 (two rows per bank row, group = 8 (r % 2) + position): swz is a
+// bijection on (r >> 1) % 8, even on rows 0-7 and odd on rows 8-15.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+    if (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
+    return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+}
+
+template <class TAG, int D, int NW, int NST, int PG>
+__global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) {
+    constexpr int ROWB = 2 * D;             // bytes per K/V/q row
+    constexpr int CPR = ROWB / 16;          // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;           // rows per direct-load instruction
+    constexpr int NI = kSlice / RPI;        // direct loads per slice, each of K and V
+    constexpr int SLB = kSlice * ROWB;      // bytes of a K (or V) slice
+    constexpr int STB = 2 * SLB;            // stage: K slice, then V slice
+    constexpr int QB = 16 * ROWB;           // q rows of the head block
+    constexpr int WAVEB = QB + NST * STB;   // LDS per wave
+    constexpr int KS = D / 32;              // k-steps of S^T = K q^T
+    constexpr int NB = D / 16;              // 16-column blocks of O
+    constexpr int PER_SLICE = 2 * NI;
+    static_assert((NST - 1) * PER_SLICE < 64, "vmcnt range");
+    static_assert((NST & (NST - 1)) == 0, "NST must be a power of two");
+    static_assert(NW * 16 * (D + 2) * 4 <= NW * WAVEB, "merge buffers must fit in the ring");
+
+    __shared__ __attribute__((aligned(1024))) char smem_raw[NW * WAVEB];
+    lds_char* smem = (lds_char*)smem_raw;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    // ---- work item: (b, split, head block, kv head), kv head fastest -------
+    const int n_hb = (a.group + 15) >> 4;
+    int id = blockIdx.x;
+    const int g = id % a.Hkv;
+    id /= a.Hkv;
+    const int hb = id % n_hb;
+    id /= n_hb;
+    const int s = id % a.n_splits;
+    const int b = id / a.n_splits;
+    const int h0 = g * a.group + hb * 16;
+    const int nh = min(16, a.group - hb * 16);
+
+    const int len = a.seq_lens[b];
+    if (len <= 0) return;
+    const int chunk = chunk_tokens(len, a.n_splits);
+    const int lo = s * chunk;
+    if (lo >= len) return;  // empty chunk: the combine kernel skips it
+    const int hi = min(len, lo + chunk);
+
+    const int stride = kSlice * NW;
+    const int span = hi - lo;
+    const int n_sl = span > kSlice * wave ? (span - kSlice * wave + stride - 1) / stride : 0;
+    const int T0 = lo + kSlice * wave;
+
+    const lds_char* wlds = smem + wave * WAVEB;
+    const uint32_t wlds_u = (uint32_t)(uintptr_t)wlds;
+
+    // per-lane constants of the direct loads: lane -> (row in instruction, physical chunk)
+    const int drow = lane / CPR;
+    const int dchk = lane % CPR;
+    int urow[NI], lcol[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        urow[i] = RPI * i + drow;
+        lcol[i] = (dchk ^ swz<D>(urow[i])) * 8;  // element offset of the logical chunk
+    }
+
+    const int* bt = a.block_table + (size_t)b * a.max_pages;
+    const int page_mask = (1 << a.page_shift) - 1;
+    const size_t tok_stride = PG == kDense ? (size_t)D : (size_t)a.Hkv * D;
+    const size_t head_off = PG == kDense ? ((size_t)b * a.Hkv + g) * (size_t)a.max_kv_len * D : (size_t)g * D;
+
+    // page ids of this wave's first 64 slices, one per lane (paged, page >= 16)
+    int pgv = 0;
+    if (PG == kPaged && lane < n_sl) pgv = bt[(T0 + stride * lane) >> a.page_shift];
+
+    // direct loads of slice k: wave-uniform base (row T of the slice) plus a
+    // per-lane byte offset; rows past the chunk repeat its last row
+    const char* kbytes = static_cast<const char*>(a.k);
+    const char* vbytes = static_cast<const char*>(a.v);
+    auto issue = [&](int k) {
+        const int T = T0 + stride * k;
+        const uint32_t st = __builtin_amdgcn_readfirstlane(wlds_u + QB + (k & (NST - 1)) * STB);
+        const int last = hi - 1 - T;  // rows of the slice at or past `last` repeat row `last`
+        if (PG == kPagedSmall) {
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const int t = T + min(urow[i], last);
+                const int page = bt[t >> a.page_shift];
+                const size_t off = ((((size_t)page << a.page_shift) + (size_t)(t & page_mask)) * tok_stride +
+                                    head_off + lcol[i]) * 2;
+                dma16(kbytes + off, st + i * 1024);
+                dma16(vbytes + off, st + SLB + i * 1024);
+            }
+            return;
+        }
+        size_t row0;  // element offset of row T
+        if (PG == kPaged) {
+            const int page = k < 64 ? __builtin_amdgcn_readlane(pgv, k)
+                                    : ((const_int*)bt)[__builtin_amdgcn_readfirstlane(T >> a.page_shift)];
+            row0 = (((size_t)page << a.page_shift) + (size_t)(T & page_mask)) * tok_stride + head_off;
+        } else {
+            row0 = head_off + (size_t)T * D;
+        }
+        const char* kb = kbytes + row0 * 2;
+        const char* vb = vbytes + row0 * 2;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const uint32_t voff = (uint32_t)(min(urow[i], last) * (int)tok_stride + lcol[i]) * 2u;
+            dma16(kb, voff, st + i * 1024);
+            dma16(vb, voff, st + SLB + i * 1024);
+        }
+    };
+
+    float m = -INFINITY, l = 0.f;
+    f32x4 acc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (n_sl > 0) {
+        // q rows of the head block (rows >= nh repeat the last head; their
+        // operand lanes are zeroed below)
+        const int nqi = (nh + RPI - 1) / RPI;
+        for (int i = 0; i < nqi; ++i) {
+            const int r = min(RPI * i + drow, nh - 1);
+            const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + h0 + r) * D +
+                                 (dchk ^ swz<D>(RPI * i + drow)) * 8;
+            dma16(qp, __builtin_amdgcn_readfirstlane(wlds_u + i * 1024));
+        }
+        const int pro = min(NST - 1, n_sl);
+        for (int k = 0; k < pro; ++k) issue(k);
+        wait_slices<PER_SLICE>(pro);
+
+        // q^T as the B operand: lane l holds head l % 16, dims 32 ks + 8 (l / 16)..+7
+        const int hrow = lane & 15;
+        const int kq = lane >> 4;
+        u32x4 qop[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const u32x4 x = lds16(wlds + hrow * ROWB + (((4 * ks + kq) ^ swz<D>(hrow)) << 4));
+            qop[ks] = hrow < nh ? x : u32x4{0u, 0u, 0u, 0u};
+        }
+        // LDS offsets of the K operand (row l % 16) and of the transposed V reads
+        int koff[KS], voff[NB];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) koff[ks] = hrow * ROWB + (((4 * ks + kq) ^ swz<D>(hrow)) << 4);
+        {
+            const int j = lane & 15;
+            const int r = 4 * kq + (j >> 2);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int c = 2 * nb + ((j & 3) >> 1);
+                voff[nb] = SLB + r * ROWB + ((c ^ swz<D>(r)) << 4) + 8 * (j & 1);
+            }
+        }
+
+        for (int k = 0; k < n_sl; ++k) {
+            if (k + NST - 1 < n_sl) issue(k + NST - 1);
+            wait_slices<PER_SLICE>(min(NST - 1, n_sl - 1 - k));
+
+            const lds_char* st = wlds + QB + (k & (NST - 1)) * STB;
+            f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) sc = mfma16x32(TAG(), lds16(st + koff[ks]), qop[ks], sc);
+
+            const int T = T0 + stride * k;
+            if (T + kSlice > hi) {  // ragged last slice of the chunk
+                const int tok = T + 4 * kq;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (tok + r >= hi) sc[r] = -INFINITY;
+            }
+            const float lm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])) * a.c;
+            if (__builtin_amdgcn_ballot_w64(lm > m + kRescaleLog2)) {
+                // new reference max for every head: max over the slice's 16 tokens
+                float mt = fmaxf(lm, shfl_xor(lm, 16));
+                mt = fmaxf(mt, xor32(mt));
+                const float mn = fmaxf(m, mt);
+                const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m - mn);
+                m = mn;
+                l *= alpha;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float ar = lane_value(alpha, 4 * kq + r);  // acc row 4 (l/16) + r is head 4 (l/16) + r
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) acc[nb][r] *= ar;
+                }
+            }
+            const float mu = m == -INFINITY ? 0.f : m;
+            float p[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p[r] = fast_exp2(fmaf(sc[r], a.c, -mu));
+            l += (p[0] + p[1]) + (p[2] + p[3]);
+            const u32x2 pop = {pack2(TAG(), p[0], p[1]), pack2(TAG(), p[2], p[3])};
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma16x16(TAG(), pop, lds_tr(st + voff[nb]), acc[nb]);
+        }
+    }
+
+    // ---- merge the NW waves' partial results -------------------------------
+    l += shfl_xor(l, 16);
+    l += xor32(l);
+    __syncthreads();  // every wave is done with its ring (and its loads have landed)
+    float* sacc = reinterpret_cast<float*>(smem_raw);  // [NW][16][D]
+    float* sm = sacc + NW * 16 * D;                    // [NW][16]
+    float* sl = sm + NW * 16;                          // [NW][16]
+    {
+        const int kq = lane >> 4, c = lane & 15;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sacc[(wave * 16 + 4 * kq + r) * D + 16 * nb + c] = acc[nb][r];
+        if (lane < 16) {
+            sm[wave * 16 + lane] = m;
+            sl[wave * 16 + lane] = l;
+        }
+    }
+    __syncthreads();
+    const size_t prow = ((size_t)b * a.Hq + h0) * a.n_splits + s;  // partial row of head h0
+    for (int i = tid; i < nh * D; i += NW * 64) {
+        const int h = i / D, d = i % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, sm[w * 16 + h]);
+        float L = 0.f, O = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float mw = sm[w * 16 + h];
+            const float e = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
+            L += e * sl[w * 16 + h];
+            O += e * sacc[(w * 16 + h) * D + d];
+        }
+        const size_t row = prow + (size_t)h * a.n_splits;
+        a.part_o[row * D + d] = O / L;
+        if (d == 0) a.part_lse[row] = (M + fast_log2(L)) * kLn2;
+    }
+}
+
+// One wave per (b, h): merge the non-empty chunks' partial results.
 template <class TAG, int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
-    constexpr int PER = D / 64;  // dims per lane
+    constexpr int PER = D / 64;  // output dims per lane
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // b * Hq + h
     if (row >= a.B * a.Hq) return;
+    const int len = a.seq_lens[row / a.Hq];
+    const int nv = len > 0 ? (len + chunk_tokens(len, a.n_splits) - 1) / chunk_tokens(len, a.n_splits) : 0;
     const float* pl = a.part_lse + (size_t)row * a.n_splits;
-    const float* po = a.part_o + (size_t)row * a.n_splits * D;
+    const float* po = a.part_o + (size_t)row * a.n_splits * D + lane * PER;
 
     float M = -INFINITY;
-    for (int s = 0; s < a.n_splits; ++s) M = fmaxf(M, pl[s]);
+    for (int s = lane; s < nv; s += 64) M = fmaxf(M, pl[s]);
+#pragma unroll
+    for (int x = 32; x >= 1; x >>= 1) M = fmaxf(M, shfl_xor(M, x));
     float W = 0.f, O[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) O[i] = 0.f;
-    if (M != -INFINITY) {
-        for (int s = 0; s < a.n_splits; ++s) {
-            const float w = fast_exp2((pl[s] - M) * kLog2e);
-            W += w;
+#pragma unroll 4
+    for (int s = 0; s < nv; ++s) {
+        const float w = fast_exp2((pl[s] - M) * kLog2e);
+        W += w;
 #pragma unroll
-            for (int i = 0; i < PER; ++i) O[i] = fmaf(w, po[(size_t)s * D + lane * PER + i], O[i]);
-        }
+        for (int i = 0; i < PER; ++i) O[i] = fmaf(w, po[(size_t)s * D + i], O[i]);
     }
     const float inv = W > 0.f ? 1.f / W : 0.f;
     uint16_t* op = static_cast<uint16_t*>(a.o) + (size_t)row * D + lane * PER;
@@ -272,12 +417,13 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     if (lane == 0) a.lse[row] = W > 0.f ? M + fast_log2(W) * kLn2 : -INFINITY;
 }
 
-template <class TAG, int D, int GH, bool PAGED>
+template <class TAG, int D, int PG>
 hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
-    const long long blocks = (long long)a.B * a.Hkv * (a.group / GH) * a.n_splits;
+    const long long n_hb = (a.group + 15) / 16;
+    const long long blocks = (long long)a.B * a.Hkv * n_hb * a.n_splits;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((decode_split_kernel<TAG, D, GH, PAGED>), dim3((unsigned)blocks), dim3(256), 0,
-                       stream, a);
+    hipLaunchKernelGGL((decode_split_kernel<TAG, D, DEC_NW, DEC_NST, PG>), dim3((unsigned)blocks),
+                       dim3(DEC_NW * 64), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_combine_kernel<TAG, D>), dim3((unsigned)((a.B * a.Hq + 3) / 4)), dim3(256),
@@ -285,18 +431,17 @@ hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <class TAG, int D, bool PAGED>
-hipError_t dispatch_group(const DecodeArgs& a, hipStream_t stream) {
-    if (a.group % 4 == 0) return launch_split<TAG, D, 4, PAGED>(a, stream);
-    if (a.group % 2 == 0) return launch_split<TAG, D, 2, PAGED>(a, stream);
-    return launch_split<TAG, D, 1, PAGED>(a, stream);
+template <class TAG, int D>
+hipError_t dispatch_layout(const DecodeArgs& a, hipStream_t stream) {
+    if (a.block_table == nullptr) return launch_split<TAG, D, kDense>(a, stream);
+    if (a.page_shift >= 4) return launch_split<TAG, D, kPaged>(a, stream);
+    return launch_split<TAG, D, kPagedSmall>(a, stream);
 }
 
 template <class TAG>
 hipError_t dispatch_d(const DecodeArgs& a, hipStream_t stream) {
-    const bool paged = a.block_table != nullptr;
-    if (a.D == 64) return paged ? dispatch_group<TAG, 64, true>(a, stream) : dispatch_group<TAG, 64, false>(a, stream);
-    return paged ? dispatch_group<TAG, 128, true>(a, stream) : dispatch_group<TAG, 128, false>(a, stream);
+    if (a.D == 64) return dispatch_layout<TAG, 64>(a, stream);
+    return dispatch_layout<TAG, 128>(a, stream);
 }
 
 }  // namespace

@@ -122,7 +122,7 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int D, int n_splits);
  * bounds-checked on the device, and an out-of-range page id or length is
  * undefined behaviour (the split-K page loads its block table unchecked too).
  *
- * Requirements: B >= 0, Hq, Hkv > 0, Hq % Hkv == 0, Hq / Hkv <= 8,
+ * Requirements: B >= 0, Hq, Hkv > 0, Hq % Hkv == 0,
  * D in {64, 128}, dtype F16 or BF16, 1 <= n_splits <= 256, max_kv_len >= 0.
  * B == 0 returns GQA_OK without launching.
  */

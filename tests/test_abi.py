@@ -97,7 +97,6 @@ def test_decode_validation(L):
     assert dec(L, max_kv_len=-1) == INVALID
     assert dec(L, D=80) == UNSUPPORTED
     assert dec(L, dtype=F32) == UNSUPPORTED
-    assert dec(L, Hq=32, Hkv=2) == UNSUPPORTED         # group of 16
     assert dec(L, q=None) == INVALID
     assert dec(L, seq=None) == INVALID
     assert dec(L, ws=None) == WORKSPACE

@@ -189,6 +189,9 @@ DECODE = [
     (2, 16, 2, 128, "bf16", 100, 2000, 64, 64),     # G = 8
     (5, 4, 2, 128, "f16", 1, 63, 1, 1),             # page size 1, one split
     (2, 6, 3, 64, "bf16", 500, 900, 128, 7),        # G = 2
+    (2, 32, 1, 128, "bf16", 100, 1500, 32, 8),      # G = 32: two blocks of 16 heads
+    (2, 20, 2, 64, "f16", 1, 400, 8, 5),            # G = 10, page size 8
+    (3, 8, 2, 128, "bf16", 2000, 5000, 16, 256),    # many splits, page size 16
 ]
 
 
