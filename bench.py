@@ -13,6 +13,7 @@ reported under "workloads".
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import platform
@@ -35,10 +36,31 @@ PEAK_HBM_GBPS = 8000.0            # MI355X HBM3E
 PRIMARY = W.CAUSAL_GQA_PREFILL
 METRIC = "attention fwd TFLOP/s + % bf16 MFMA peak; decode GB/s + % HBM peak"
 
-# HBM traffic per launch of the dominant kernel from rocprofv3 --pmc
-# (FETCH_SIZE, WRITE_SIZE, KiB per dispatch), scaled by the same counters on a
-# copy of known size; None until counters are taken for the current kernel.
-MEASURED_TRAFFIC_BYTES = None
+# HBM traffic per launch of the dominant kernel: rocprofv3 --pmc FETCH_SIZE and
+# WRITE_SIZE (KiB per dispatch, one pass each, profiles/prefill_fwd_pp_causal_gqa_prefill.md),
+# scaled by what the same counters read for `--only hbm_copy` (COPY_BYTES read
+# and written).  The figures hold for the kernel source they were taken on; any
+# other source reports traffic null.
+TRAFFIC_MEASUREMENT = {
+    "source": "gqa_attention_forward_attn_amd/csrc/prefill_pp.hip",
+    "sha1": "e6ccc9f0dd6a5936eef54c67904aaad5baa84de2",
+    "fetch_kib": 26649.6, "write_kib": 33280.0,
+    "copy_fetch_kib": 262156.0, "copy_write_kib": 524288.0,
+}
+
+
+def measured_traffic():
+    m = TRAFFIC_MEASUREMENT
+    try:
+        with open(os.path.join(ROOT, m["source"]), "rb") as f:
+            if hashlib.sha1(f.read()).hexdigest() != m["sha1"]:
+                return None
+    except OSError:
+        return None
+    copy_kib = COPY_BYTES / 1024
+    fetch = m["fetch_kib"] * 1024 * copy_kib / m["copy_fetch_kib"]
+    write = m["write_kib"] * 1024 * copy_kib / m["copy_write_kib"]
+    return int(round(fetch + write))
 
 
 def visible_pairs(q_len: int, kv_len: int, causal: bool) -> int:
@@ -64,25 +86,34 @@ def decode_bytes(spec, inp) -> int:
 
 
 def time_launches(fn, steps: int, warmup: int):
-    """Warm up, then time `steps` calls: wall time around the whole loop
-    (synchronize on both sides) and a HIP event pair around every call on the
-    stream the library launches on (torch's current stream)."""
+    """Warm up, then time `steps` back-to-back calls: wall time around the loop
+    (synchronize on both sides) and one HIP event pair around it on the stream
+    the library launches on (torch's current stream), whose span / steps is the
+    mean launch duration.  A second pass with an event pair around every call
+    gives the spread (min, p90); those pairs also hold the dispatch gap."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mean = start.elapsed_time(end) * 1e-3 / steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     for i in range(steps):
         starts[i].record(stream)
         fn()
         ends[i].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]) * 1e-3
-    return wall, per
+    return wall, mean, per
 
 
 def bench_prefill(spec, steps, warmup):
@@ -96,10 +127,9 @@ def bench_prefill(spec, steps, warmup):
     def step():
         gqa.attn_fwd(q, k, v, causal=spec.causal, scale=scale, out=o, lse=lse)
 
-    wall, per = time_launches(step, steps, warmup)
+    wall, kern_s, per = time_launches(step, steps, warmup)
     flops = prefill_flops(spec)
     peak = PEAK_MFMA_F32_TFLOPS if spec.dtype == "f32" else PEAK_MFMA_16BIT_TFLOPS
-    kern_s = float(np.mean(per))
     return {
         "workload": spec.name, "dtype": spec.dtype, "causal": spec.causal,
         "shape": {"B": spec.B, "Hq": spec.Hq, "Hkv": spec.Hkv, "q_len": spec.q_len,
@@ -113,6 +143,20 @@ def bench_prefill(spec, steps, warmup):
         "peak_tflops": peak,
         "frac_of_peak": flops / kern_s / 1e12 / peak,
     }
+
+
+COPY_BYTES = 512 << 20
+
+
+def bench_copy(steps, warmup):
+    """Calibration for the hardware byte counters: a plain device-to-device copy
+    of COPY_BYTES (read COPY_BYTES, write COPY_BYTES) per call."""
+    dev = torch.device("cuda:0")
+    x = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).uniform_()
+    y = torch.empty_like(x)
+    wall, kern_s, per = time_launches(lambda: y.copy_(x), steps, warmup)
+    return {"workload": "hbm_copy", "bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
+            "kernel_ms_mean": kern_s * 1e3, "gbps": 2 * COPY_BYTES / kern_s / 1e9}
 
 
 def bench_decode(spec, steps, warmup):
@@ -131,9 +175,8 @@ def bench_decode(spec, steps, warmup):
         gqa.attn_decode_splitk(q, kc, vc, sl, block_table=bt, n_splits=spec.n_splits, scale=scale,
                                max_kv_len=inp.max_kv_len, workspace=ws, out=o, lse=lse)
 
-    wall, per = time_launches(step, steps, warmup)
+    wall, kern_s, per = time_launches(step, steps, warmup)
     nbytes = decode_bytes(spec, inp)
-    kern_s = float(np.mean(per))
     return {
         "workload": spec.name, "dtype": spec.dtype,
         "shape": {"B": spec.B, "Hq": spec.Hq, "Hkv": spec.Hkv, "D": spec.D,
@@ -187,7 +230,9 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default=None, help="time only this workload (profiling runs)")
+    ap.add_argument("--only", default=None,
+                    help="time only this workload (profiling runs); 'hbm_copy' times a plain copy "
+                         "used to calibrate the HBM byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -200,6 +245,9 @@ def main():
 
     all_specs = [W.CAUSAL_GQA_FP32, W.CAUSAL_GQA_PREFILL, W.CAUSAL_GQA_OFFSET,
                  W.MHA_NONCAUSAL_FP16, W.PAGED_DECODE]
+    if args.only == "hbm_copy":
+        print(json.dumps(bench_copy(args.steps, args.warmup)), flush=True)
+        return
     if args.only:
         specs = [s for s in all_specs if s.name == args.only]
         if not specs:
@@ -244,8 +292,8 @@ def main():
             "peak": PEAK_MFMA_16BIT_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(p["frac_of_peak"], 4),
-            "traffic": MEASURED_TRAFFIC_BYTES,
-            "kernel": "prefill_fwd_mfma<bf16, D=128, causal, 4 heads/workgroup>",
+            "traffic": measured_traffic(),
+            "kernel": "prefill_fwd_pp<bf16, D=128, causal, 4 heads/workgroup>",
             "kernel_ms_mean": round(p["kernel_ms_mean"], 5),
         },
         "workloads": results,

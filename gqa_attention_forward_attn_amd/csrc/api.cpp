@@ -5,6 +5,8 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
+#include <cstring>
 
 #include <hip/hip_runtime.h>
 
@@ -27,6 +29,16 @@ int to_kernel_dtype(gqa_dtype_t t) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// bf16 / fp16 prefill kernel.  By default the library picks by shape; the
+// environment variable GQA_ATTN_PREFILL_KERNEL=pingpong|fourwave forces one
+// (read at every call, for tests that cover both kernels on the same shapes).
+gqa::PrefillKernel prefill_kernel_choice() {
+    const char* v = std::getenv("GQA_ATTN_PREFILL_KERNEL");
+    if (v && std::strcmp(v, "pingpong") == 0) return gqa::PrefillKernel::kPingPong;
+    if (v && std::strcmp(v, "fourwave") == 0) return gqa::PrefillKernel::kFourWave;
+    return gqa::PrefillKernel::kAuto;
+}
 
 }  // namespace
 
@@ -57,7 +69,7 @@ gqa_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, floa
     a.group = Hq / Hkv;
     a.delta = kv_len - q_len;
     a.c = scale * kLog2e;
-    hipError_t e = gqa::launch_prefill(a, D, causal != 0, to_kernel_dtype(dtype),
+    hipError_t e = gqa::launch_prefill(a, D, causal != 0, to_kernel_dtype(dtype), prefill_kernel_choice(),
                                        static_cast<hipStream_t>(hip_stream));
     return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }

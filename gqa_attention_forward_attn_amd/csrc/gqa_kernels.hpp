@@ -25,8 +25,11 @@ struct PrefillArgs {
     float c;          // scale * log2(e)
 };
 
+// bf16 / fp16 prefill kernel: chosen by shape, or forced (tests).
+enum class PrefillKernel { kAuto, kPingPong, kFourWave };
+
 // Validated arguments only.  D in {64, 128}; dtype one of kDtype*.
-hipError_t launch_prefill(PrefillArgs a, int D, bool causal, int dtype, hipStream_t stream);
+hipError_t launch_prefill(PrefillArgs a, int D, bool causal, int dtype, PrefillKernel kernel, hipStream_t stream);
 // Ping-pong schedule, 8 waves x 32 rows (bf16 / fp16 only).
 hipError_t launch_prefill_pp(PrefillArgs a, int D, bool causal, int dtype, hipStream_t stream);
 

@@ -485,8 +485,19 @@ hipError_t dispatch_d(PrefillArgs a, int D, bool causal, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_prefill(PrefillArgs a, int D, bool causal, int dtype, hipStream_t stream) {
-    if (dtype != kDtypeF32) return launch_prefill_pp(a, D, causal, dtype, stream);
+hipError_t launch_prefill(PrefillArgs a, int D, bool causal, int dtype, PrefillKernel kernel, hipStream_t stream) {
+    if (dtype != kDtypeF32 && kernel == PrefillKernel::kAuto) {
+        // the ping-pong kernel owns 256 (query, head) rows per workgroup and runs
+        // one workgroup per CU; below one workgroup per CU the four-wave kernel
+        // (128 rows, two workgroups per CU) keeps more of the chip busy
+        int dev = 0, n_cu = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        const long long rows = (long long)a.B * a.Hq * a.q_len;
+        kernel = rows >= 256LL * n_cu ? PrefillKernel::kPingPong : PrefillKernel::kFourWave;
+    }
+    if (dtype != kDtypeF32 && kernel == PrefillKernel::kPingPong) return launch_prefill_pp(a, D, causal, dtype, stream);
     switch (dtype) {
     case kDtypeBF16: return dispatch_d<bf16_tag>(a, D, causal, stream);
     case kDtypeF16: return dispatch_d<f16_tag>(a, D, causal, stream);

@@ -63,10 +63,16 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "-".join(map(str, s)))
-def test_prefill_all_elements(shape):
+# bf16 / fp16 prefill has two kernels (chosen by shape); every shape runs on both
+PREFILL_KERNELS = ["pingpong", "fourwave"]
+SMALL_CASES = [(s, kern) for s in SMALL for kern in (PREFILL_KERNELS if s[6] != "f32" else ["auto"])]
+
+
+@pytest.mark.parametrize("shape,kernel", SMALL_CASES, ids=lambda c: "-".join(map(str, c)) if isinstance(c, tuple) else c)
+def test_prefill_all_elements(shape, kernel, monkeypatch):
+    monkeypatch.setenv("GQA_ATTN_PREFILL_KERNEL", kernel)
     B, Hq, Hkv, Lq, Lk, D, dt, causal = shape
-    print(f"prefill case {shape}", flush=True)
+    print(f"prefill case {shape} kernel {kernel}", flush=True)
     q, k, v = W.make_prefill(B, Hq, Hkv, Lq, Lk, D, dt, seed=sum(shape[:6]))
     scale = W.fp32_scale(D)
     o, l = gpu_fwd(q, k, v, causal, scale)
@@ -98,9 +104,15 @@ def sample_rows(B, Hq, Lq, n_random, seed):
     return np.unique(np.array(rows, dtype=np.int64))
 
 
-@pytest.mark.parametrize("spec", W.PREFILL_WORKLOADS, ids=lambda s: s.name)
-def test_prefill_workload_sampled(spec):
-    print(f"workload {spec.name}", flush=True)
+WORKLOAD_CASES = [(s, kern) for s in W.PREFILL_WORKLOADS
+                  for kern in (PREFILL_KERNELS if s.dtype != "f32" else ["auto"])]
+
+
+@pytest.mark.parametrize("spec,kernel", WORKLOAD_CASES,
+                         ids=lambda c: c.name if hasattr(c, "name") else c)
+def test_prefill_workload_sampled(spec, kernel, monkeypatch):
+    monkeypatch.setenv("GQA_ATTN_PREFILL_KERNEL", kernel)
+    print(f"workload {spec.name} kernel {kernel}", flush=True)
     q, k, v = W.make_prefill_spec(spec)
     scale = W.fp32_scale(spec.D)
     o, l = gpu_fwd(q, k, v, spec.causal, scale)
