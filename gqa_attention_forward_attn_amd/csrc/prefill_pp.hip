@@ -51,7 +51,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 // from moving LDS accesses across it.
 __device__ __forceinline__ void barrier_no_fence() {
     __asm__ __volatile__("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);  // no instruction moves across a phase boundary
     __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
     __asm__ __volatile__("" ::: "memory");
 }
 
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int grp = wave >> 2;             // ping-pong group: 0 leads, 1 trails by one phase
+    const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);             // ping-pong group: 0 leads, 1 trails by one phase
     const int half = lane >> 5;
     const int l32 = lane & 31;
 
@@ -330,16 +332,19 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
         l += ls;
     };
 
-    // ---- phase loop ----------------------------------------------------------------
-    // Phase p: group 0 runs the MFMA phase of tile p/2 when p is even and the
-    // VALU phase of tile p/2 when p is odd; group 1 runs the same one phase
-    // later.  Every wave passes one barrier per phase.
+    // ---- phase sequence ------------------------------------------------------------
+    // Global phase p: group 0 runs step q = p of its sequence, group 1 step
+    // q = p - 1; every wave passes one barrier per phase (2 n_tiles + 2 in all).
+    // A wave's own steps: scores of tile 0, then (softmax of tile t, MFMAs of
+    // tile t+1: scores of t+1 and P.V of t) for each t, the last P.V alone.
+    // Tile t must be in LDS (this wave's loads done, then the barrier) from
+    // phase 2t on; tile t+2 is issued right after the barrier of phase 2t.
     if (n_tiles > 0) {
         issue_tile(0);
         if (n_tiles > 1) issue_tile(1);
-        const int n_phases = 2 * n_tiles + 2;
-        for (int p = 0; p < n_phases; ++p) {
-            if ((p & 1) == 0) {  // tile p/2 is read from this phase on
+        int p = 0;
+        auto sync = [&]() {
+            if ((p & 1) == 0) {
                 const int t = p >> 1;
                 if (t < n_tiles) {
                     if (t + 1 < n_tiles) wait_vmcnt<2 * LPW>(); else wait_vmcnt<0>();
@@ -347,14 +352,22 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
             }
             barrier_no_fence();
             if ((p & 1) == 0 && (p >> 1) + 2 < n_tiles) issue_tile((p >> 1) + 2);
-            const int q = p - grp;
-            if (q < 0 || q > 2 * n_tiles) continue;
-            const int t = q >> 1;
-            if (q & 1) valu_phase(t);
-            else if (t == 0) scores_only(0);
-            else if (t == n_tiles) pv_only(t);
-            else mfma_phase(t);
+            ++p;
+        };
+        if (grp) sync();  // group 1 starts one phase later
+        sync();
+        scores_only(0);
+        for (int t = 0; t + 1 < n_tiles; ++t) {
+            sync();
+            valu_phase(t);
+            sync();
+            mfma_phase(t + 1);
         }
+        sync();
+        valu_phase(n_tiles - 1);
+        sync();
+        pv_only(n_tiles);
+        if (!grp) sync();  // group 0 waits out the last phase of group 1
     }
 
     // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----------------------------
