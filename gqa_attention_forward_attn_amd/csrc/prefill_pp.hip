@@ -67,6 +67,12 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
                          : "m0");
 }
 
+// Marks a register value as consumed here.  The softmax arithmetic is pure
+// and feeds only the next phase's MFMAs, so without this the compiler sinks it
+// across the phase barrier into the MFMA phase.
+__device__ __forceinline__ void pin(uint32_t& x) { __asm__ __volatile__("" : "+v"(x)); }
+__device__ __forceinline__ void pin(float& x) { __asm__ __volatile__("" : "+v"(x)); }
+
 __device__ __forceinline__ u32x2 lds_read_tr(const lds_char* p) {
     i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
     return __builtin_bit_cast(u32x2, v);
@@ -330,6 +336,10 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
                 ls += p0 + p1;  // row sum of the unrounded weights
             }
         l += ls;
+        // the weights are computed here, in the VALU phase, not next to the MFMAs that use them
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pin(pk[i]);
+        pin(l);
     };
 
     // ---- phase sequence ------------------------------------------------------------
