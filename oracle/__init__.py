@@ -67,6 +67,9 @@ def _load():
                                               i32, i32, i32, f64, vp, i32, vp, i64, vp, vp,
                                               vp, vp]
     lib.oracle_decode_split_merge.restype = i32
+    lib.oracle_attn_decode_multi.argtypes = [vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
+                                             i32, i32, i32, f64, vp, i64, vp, vp]
+    lib.oracle_attn_decode_multi.restype = i32
     _lib = lib
     return lib
 
@@ -161,7 +164,7 @@ def softmax_matrix(q, k, scale: float, causal: bool, b: int, h: int) -> np.ndarr
 def _decode_common(q, k, v, seq_lens, block_table, max_kv_len):
     q, k, v = _cpu(q), _cpu(k), _cpu(v)
     dt = _dt(q, k, v)
-    B, Hq, D = q.shape
+    B, Hq, D = q.shape[0], q.shape[1], q.shape[-1]
     sl = _cpu(seq_lens, torch.int32)
     if block_table is not None:
         bt = _cpu(block_table, torch.int32)
@@ -226,3 +229,28 @@ def decode_split_merge(q, k, v, seq_lens, scale: float, bounds, block_table=None
     if rc:
         raise ValueError("oracle_decode_split_merge: bad arguments")
     return o, lse, op, lp
+
+
+def attn_decode_multi(q, k, v, seq_lens, scale: float, block_table=None, max_kv_len=None, rows=None):
+    """Decode of q_len queries per sequence, placed at its last q_len positions
+    (query i sees keys t <= seq_lens[b] - q_len + i).
+
+    q [B, Hq, q_len, D]; K/V as for attn_decode.  Returns (o [B, Hq, q_len, D],
+    lse [B, Hq, q_len]) or, with rows, (o [n, D], lse [n]) for flat ids
+    (b*Hq + h)*q_len + i.
+    """
+    q, k, v, dt, B, Hq, D, sl, bt, max_pages, page_size, Hkv, max_kv_len = _decode_common(
+        q, k, v, seq_lens, block_table, max_kv_len)
+    q_len = q.shape[2]
+    r = _rows(rows)
+    n = B * Hq * q_len if r is None else r.shape[0]
+    o = np.empty((n, D), dtype=np.float64)
+    lse = np.empty((n,), dtype=np.float64)
+    rc = _load().oracle_attn_decode_multi(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(sl), _ptr(bt), max_pages,
+                                          page_size, B, Hq, Hkv, q_len, D, max_kv_len, float(scale),
+                                          _np_ptr(r), n, _np_ptr(o), _np_ptr(lse))
+    if rc:
+        raise ValueError("oracle_attn_decode_multi: bad arguments")
+    if r is None:
+        return o.reshape(B, Hq, q_len, D), lse.reshape(B, Hq, q_len)
+    return o, lse

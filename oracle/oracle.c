@@ -287,6 +287,54 @@ int oracle_attn_decode(const void* q, const void* k, const void* v, int dt,
 }
 
 /*
+ * Decode with q_len queries per sequence.  [P4] `_fwd_kernel_splitK` with
+ * IS_CAUSAL and NUM_QUERIES_CAUSAL: the queries of sequence b sit at its last
+ * q_len positions, so query i has position seq_lens[b] - q_len + i and sees
+ * the keys at or before it; a query before the first key sees none.
+ *
+ * q is [B, Hq, q_len, D]; rows are flat ((b * Hq + h) * q_len + i) ids (NULL
+ * = all).  K/V addressing as in oracle_attn_decode.  o_out [n_rows, D],
+ * lse_out [n_rows].
+ */
+int oracle_attn_decode_multi(const void* q, const void* k, const void* v, int dt,
+                             const int* seq_lens, const int* block_table, int max_pages,
+                             int page_size, int B, int Hq, int Hkv, int q_len, int D,
+                             int max_kv_len, double scale, const int64_t* rows, int64_t n_rows,
+                             double* o_out, double* lse_out) {
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv || max_kv_len < 0 || q_len <= 0) return 1;
+    if (block_table && (page_size <= 0 || max_pages <= 0)) return 1;
+    const int64_t total = (int64_t)B * Hq * q_len;
+    if (!rows) n_rows = total;
+    const int group = Hq / Hkv;
+    int bad = 0;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)(max_kv_len > 0 ? max_kv_len : 1));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t n = 0; n < n_rows; ++n) {
+            int64_t r = rows ? rows[n] : n;
+            if (r < 0 || r >= total) { bad = 1; continue; }
+            int64_t i = r % q_len;
+            int64_t bh = r / q_len;
+            int h = (int)(bh % Hq);
+            int b = (int)(bh / Hq);
+            int g = h / group;
+            int64_t len = seq_lens[b];
+            if (len < 0 || len > max_kv_len) { bad = 1; continue; }
+            kv_view kv = {k, v, dt, D, ((int64_t)b * Hkv + g) * max_kv_len * (int64_t)D,
+                          block_table ? block_table + (int64_t)b * max_pages : NULL,
+                          page_size, Hkv, g};
+            /* position of query i: len - q_len + i; keys t <= that position */
+            int64_t vis_end = len - q_len + i + 1;
+            attend_one(q, r * (int64_t)D, dt, &kv, 0, len, vis_end, scale, s,
+                       o_out + n * (int64_t)D, lse_out + n, NULL);
+        }
+        free(s);
+    }
+    return bad;
+}
+
+/*
  * Split-K decode by the split/merge route, for the invariant tests.
  * bounds is [B, n_splits + 1]: chunk s of sequence b covers tokens
  * [bounds[b][s], bounds[b][s+1]) clipped to seq_lens[b].  Each chunk's

@@ -351,3 +351,40 @@ def test_split_merge_all_empty():
     o, l, _, _ = oracle.decode_split_merge(inp.q, inp.k_cache, inp.v_cache, inp.seq_lens, 0.3,
                                            [[0, 4, 8]], block_table=inp.block_table)
     assert np.all(o == 0) and np.all(l == -np.inf)
+
+
+# ---- several queries per sequence ---------------------------------------------
+
+def test_decode_multi_query_i_is_decode_of_a_prefix():
+    # Query i sits at position len - q_len + i, so it is plain decode over the
+    # first len - q_len + 1 + i keys (none if that is <= 0).
+    q_len = 5
+    inp = make_decode(3, 8, 2, 16, "f32", seed=22, len_lo=2, len_hi=40, page_size=8, q_len=q_len)
+    o, l = oracle.attn_decode_multi(inp.q, inp.k_cache, inp.v_cache, inp.seq_lens, 0.3,
+                                    block_table=inp.block_table)
+    for i in range(q_len):
+        lens_i = torch.clamp(inp.seq_lens - (q_len - 1 - i), min=0).to(torch.int32)
+        oi, li = oracle.attn_decode(inp.q[:, :, i].contiguous(), inp.k_cache, inp.v_cache, lens_i, 0.3,
+                                    block_table=inp.block_table)
+        assert np.array_equal(o[:, :, i], oi) and np.array_equal(l[:, :, i], li)
+
+
+@pytest.mark.parametrize("q_len,dtype", [(1, "f32"), (6, "f32"), (3, "bf16")])
+def test_decode_multi_matches_torch_reference(q_len, dtype):
+    # Against torch fp64 with an explicit bottom-right mask over a dense copy of
+    # each sequence's keys, gathered here from the pool; sequences shorter than
+    # q_len leave their leading queries with no visible key (o = 0, lse = -inf).
+    inp = make_decode(4, 8, 2, 16, dtype, seed=23 + q_len, len_lo=1, len_hi=40, page_size=8, q_len=q_len)
+    scale = 0.25
+    o, l = oracle.attn_decode_multi(inp.q, inp.k_cache, inp.v_cache, inp.seq_lens, scale,
+                                    block_table=inp.block_table)
+    for b in range(4):
+        n = int(inp.seq_lens[b])
+        pages = inp.block_table[b, :(n + 7) // 8].long()
+        kd = inp.k_cache[pages].reshape(-1, 2, 16)[:n].permute(1, 0, 2).unsqueeze(0).contiguous()
+        vd = inp.v_cache[pages].reshape(-1, 2, 16)[:n].permute(1, 0, 2).unsqueeze(0).contiguous()
+        o_ref, l_ref = torch_reference(inp.q[b:b + 1], kd, vd, scale, True)
+        np.testing.assert_allclose(o[b], o_ref[0], atol=TOL, rtol=0)
+        np.testing.assert_array_equal(np.isinf(l[b]), np.isinf(l_ref[0]))
+        fin = np.isfinite(l_ref[0])
+        np.testing.assert_allclose(l[b][fin], l_ref[0][fin], atol=TOL, rtol=0)

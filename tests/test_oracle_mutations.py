@@ -35,6 +35,10 @@ MUTANTS = {
     "merge_lse_dropped_max": ("lse_out[n] = M + log(wsum);", "lse_out[n] = log(wsum);"),
     "half_exponent_bias": ("v = ldexp((double)(m | 0x400), e - 25);", "v = ldexp((double)(m | 0x400), e - 24);"),
     "bf16_shift": ("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;"),
+    "multi_query_position_off_by_one": ("int64_t vis_end = len - q_len + i + 1;",
+                                        "int64_t vis_end = len - q_len + i;"),
+    "multi_query_order_reversed": ("int64_t vis_end = len - q_len + i + 1;",
+                                   "int64_t vis_end = len - i;"),
 }
 
 

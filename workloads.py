@@ -15,6 +15,7 @@ Workloads (shapes of the attention problems the pages state):
   mha_noncausal_fp16    B=4 H=16 S=4096 D=64, fp16, inputs x0.5, non-causal
   paged_decode          B=16 Hq=32 Hkv=8 D=128, bf16, kv_len ~ U[1024, 32768],
                         256-token pages placed by a seeded permutation, 16 splits
+  multi_query_decode    the same with 4 queries per sequence at its last positions
 """
 from __future__ import annotations
 
@@ -62,6 +63,7 @@ class DecodeSpec:
     max_pages: int
     n_splits: int
     seed: int
+    q_len: int = 1       # queries per sequence (its last positions); 1 is plain decode
 
 
 CAUSAL_GQA_FP32 = PrefillSpec("causal_gqa_fp32", 1, 4, 2, 128, 128, 64, "f32", True, 20261)
@@ -69,6 +71,8 @@ CAUSAL_GQA_PREFILL = PrefillSpec("causal_gqa_prefill", 2, 32, 8, 2048, 2048, 128
 CAUSAL_GQA_OFFSET = PrefillSpec("causal_gqa_offset", 1, 32, 4, 1024, 4096, 128, "bf16", True, 20263)
 MHA_NONCAUSAL_FP16 = PrefillSpec("mha_noncausal_fp16", 4, 16, 16, 4096, 4096, 64, "f16", False, 20264, 0.5)
 PAGED_DECODE = DecodeSpec("paged_decode", 16, 32, 8, 128, "bf16", 1024, 32768, 256, 128, 16, 20265)
+MULTI_QUERY_DECODE = DecodeSpec("multi_query_decode", 16, 32, 8, 128, "bf16", 1024, 32768, 256, 128, 16,
+                                20266, q_len=4)
 
 PREFILL_WORKLOADS = [CAUSAL_GQA_FP32, CAUSAL_GQA_PREFILL, CAUSAL_GQA_OFFSET, MHA_NONCAUSAL_FP16]
 
@@ -97,7 +101,7 @@ def make_prefill_spec(spec: PrefillSpec):
 
 @dataclass
 class DecodeInputs:
-    q: torch.Tensor            # [B, Hq, D]
+    q: torch.Tensor            # [B, Hq, D], or [B, Hq, q_len, D] when q_len is given
     k_cache: torch.Tensor      # [num_pages, page_size, Hkv, D]
     v_cache: torch.Tensor
     seq_lens: torch.Tensor     # [B] int32
@@ -107,7 +111,7 @@ class DecodeInputs:
 
 
 def make_decode(B, Hq, Hkv, D, dtype="bf16", seed=0, len_lo=1, len_hi=64, page_size=256,
-                max_pages: Optional[int] = None, seq_lens=None, permute=True):
+                max_pages: Optional[int] = None, seq_lens=None, permute=True, q_len: Optional[int] = None):
     """Paged decode inputs, drawn in the order q, seq_lens, page permutation, K, V.
 
     Sequence b uses n_b = ceil(len_b / page_size) pages; pages are handed out
@@ -116,7 +120,7 @@ def make_decode(B, Hq, Hkv, D, dtype="bf16", seed=0, len_lo=1, len_hi=64, page_s
     """
     g = torch.Generator().manual_seed(seed)
     dt = _DTYPES[dtype]
-    q = _randn((B, Hq, D), g, dt)
+    q = _randn((B, Hq, D) if q_len is None else (B, Hq, q_len, D), g, dt)
     if seq_lens is None:
         seq_lens = torch.randint(len_lo, len_hi + 1, (B,), generator=g, dtype=torch.int64)
     seq_lens = torch.as_tensor(seq_lens, dtype=torch.int64)
@@ -139,5 +143,6 @@ def make_decode(B, Hq, Hkv, D, dtype="bf16", seed=0, len_lo=1, len_hi=64, page_s
 
 def make_decode_spec(spec: DecodeSpec):
     return make_decode(spec.B, spec.Hq, spec.Hkv, spec.D, spec.dtype, spec.seed,
-                       spec.len_lo, spec.len_hi, spec.page_size, spec.max_pages)
+                       spec.len_lo, spec.len_hi, spec.page_size, spec.max_pages,
+                       q_len=None if spec.q_len == 1 else spec.q_len)
 
