@@ -79,8 +79,8 @@ def decode_bytes(spec, inp) -> int:
     tokens = int(inp.seq_lens.to(torch.int64).sum())
     pages = int(sum((int(s) + spec.page_size - 1) // spec.page_size for s in inp.seq_lens))
     kv = 2 * tokens * spec.Hkv * spec.D * elt
-    qo = 2 * spec.B * spec.Hq * spec.D * elt
-    lse = spec.B * spec.Hq * 4
+    qo = 2 * spec.B * spec.Hq * spec.q_len * spec.D * elt
+    lse = spec.B * spec.Hq * spec.q_len * 4
     meta = 4 * pages + 4 * spec.B
     return kv + qo + lse + meta
 
@@ -166,24 +166,25 @@ def bench_decode(spec, steps, warmup):
     kc, vc = inp.k_cache.to(dev), inp.v_cache.to(dev)
     sl, bt = inp.seq_lens.to(dev), inp.block_table.to(dev)
     o = torch.empty_like(q)
-    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
-    ws = torch.empty(gqa.decode_workspace_bytes(spec.B, spec.Hq, spec.D, spec.n_splits),
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+    ws = torch.empty(gqa.decode_workspace_bytes_multi(spec.B, spec.Hq, spec.q_len, spec.D, spec.n_splits),
                      dtype=torch.uint8, device=dev)
     scale = W.fp32_scale(spec.D)
+    call = gqa.attn_decode_splitk if spec.q_len == 1 else gqa.attn_decode_splitk_multi
 
     def step():
-        gqa.attn_decode_splitk(q, kc, vc, sl, block_table=bt, n_splits=spec.n_splits, scale=scale,
-                               max_kv_len=inp.max_kv_len, workspace=ws, out=o, lse=lse)
+        call(q, kc, vc, sl, block_table=bt, n_splits=spec.n_splits, scale=scale,
+             max_kv_len=inp.max_kv_len, workspace=ws, out=o, lse=lse)
 
     wall, kern_s, per = time_launches(step, steps, warmup)
     nbytes = decode_bytes(spec, inp)
     return {
         "workload": spec.name, "dtype": spec.dtype,
-        "shape": {"B": spec.B, "Hq": spec.Hq, "Hkv": spec.Hkv, "D": spec.D,
+        "shape": {"B": spec.B, "Hq": spec.Hq, "Hkv": spec.Hkv, "D": spec.D, "q_len": spec.q_len,
                   "page_size": spec.page_size, "n_splits": spec.n_splits,
                   "sum_kv_len": int(inp.seq_lens.to(torch.int64).sum())},
         "bytes_per_step": nbytes,
-        "workspace_bytes_rw": 2 * spec.B * spec.Hq * spec.n_splits * (spec.D + 1) * 4,
+        "workspace_bytes_rw": 2 * spec.B * spec.Hq * spec.q_len * spec.n_splits * (spec.D + 1) * 4,
         "ms_per_step": wall / steps * 1e3,
         "kernel_ms_mean": kern_s * 1e3, "kernel_ms_min": float(per.min()) * 1e3,
         "gbps": nbytes * steps / wall / 1e9,
@@ -244,7 +245,7 @@ def main():
         sys.exit(2)
 
     all_specs = [W.CAUSAL_GQA_FP32, W.CAUSAL_GQA_PREFILL, W.CAUSAL_GQA_OFFSET,
-                 W.MHA_NONCAUSAL_FP16, W.PAGED_DECODE]
+                 W.MHA_NONCAUSAL_FP16, W.PAGED_DECODE, W.MULTI_QUERY_DECODE]
     if args.only == "hbm_copy":
         print(json.dumps(bench_copy(args.steps, args.warmup)), flush=True)
         return

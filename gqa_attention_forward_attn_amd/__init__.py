@@ -23,7 +23,8 @@ STATUS = {0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_UNSUPPORTED",
 _TORCH_DT = {torch.float32: GQA_F32, torch.float16: GQA_F16, torch.bfloat16: GQA_BF16}
 
 # Every symbol include/gqa_attn.h declares.
-EXPORTS = ("attn_fwd", "attn_decode_workspace_bytes", "attn_decode_splitk", "attn_status_str")
+EXPORTS = ("attn_fwd", "attn_decode_workspace_bytes", "attn_decode_splitk",
+           "attn_decode_workspace_bytes_multi", "attn_decode_splitk_multi", "attn_status_str")
 
 _lib = None
 
@@ -51,6 +52,11 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_splitk.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                      f32, i32, vp, sz, i32, vp]
     L.attn_decode_splitk.restype = i32
+    L.attn_decode_workspace_bytes_multi.argtypes = [i32, i32, i32, i32, i32]
+    L.attn_decode_workspace_bytes_multi.restype = sz
+    L.attn_decode_splitk_multi.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                           i32, f32, i32, vp, sz, i32, vp]
+    L.attn_decode_splitk_multi.restype = i32
     L.attn_status_str.argtypes = [i32]
     L.attn_status_str.restype = ctypes.c_char_p
     _lib = L
@@ -106,18 +112,7 @@ def decode_workspace_bytes(B: int, Hq: int, D: int, n_splits: int) -> int:
     return int(lib().attn_decode_workspace_bytes(B, Hq, D, n_splits))
 
 
-def attn_decode_splitk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens: torch.Tensor,
-                       block_table: Optional[torch.Tensor] = None, n_splits: int = 16,
-                       scale: Optional[float] = None, max_kv_len: Optional[int] = None,
-                       workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                       lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Split-K decode. q [B,Hq,D]; paged k/v [pages,page_size,Hkv,D] with block_table
-    [B,max_pages] int32, or dense k/v [B,Hkv,max_kv_len,D] with block_table None.
-
-    Returns (o [B,Hq,D], lse [B,Hq] fp32).  `workspace` (uint8, >= decode_workspace_bytes)
-    may be passed to avoid an allocation per call.
-    """
-    B, Hq, D = q.shape
+def _decode_layout(k, block_table, max_kv_len):
     if block_table is not None:
         _, page_size, Hkv, _ = k.shape
         max_pages = block_table.shape[1]
@@ -130,10 +125,30 @@ def attn_decode_splitk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_le
         page_size, max_pages = 0, 0
         if max_kv_len is None:
             max_kv_len = L
+    return Hkv, page_size, max_pages, int(max_kv_len)
+
+
+def _decode_checks(q, k, v, seq_lens):
     if seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous():
         raise TypeError("seq_lens must be a contiguous int32 tensor")
     if q.dtype not in _TORCH_DT or k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share one dtype")
+
+
+def attn_decode_splitk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens: torch.Tensor,
+                       block_table: Optional[torch.Tensor] = None, n_splits: int = 16,
+                       scale: Optional[float] = None, max_kv_len: Optional[int] = None,
+                       workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                       lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Split-K decode. q [B,Hq,D]; paged k/v [pages,page_size,Hkv,D] with block_table
+    [B,max_pages] int32, or dense k/v [B,Hkv,max_kv_len,D] with block_table None.
+
+    Returns (o [B,Hq,D], lse [B,Hq] fp32).  `workspace` (uint8, >= decode_workspace_bytes)
+    may be passed to avoid an allocation per call.
+    """
+    B, Hq, D = q.shape
+    Hkv, page_size, max_pages, max_kv_len = _decode_layout(k, block_table, max_kv_len)
+    _decode_checks(q, k, v, seq_lens)
     need = decode_workspace_bytes(B, Hq, D, n_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
@@ -144,8 +159,43 @@ def attn_decode_splitk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_le
     sc = default_scale(D) if scale is None else float(scale)
     rc = lib().attn_decode_splitk(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(seq_lens),
                                   _ptr(block_table), max_pages, page_size, B, Hq, Hkv, D,
-                                  int(max_kv_len), sc, int(n_splits), _ptr(workspace),
+                                  max_kv_len, sc, int(n_splits), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(),
                                   _TORCH_DT[q.dtype], _stream(q.device))
     _check("attn_decode_splitk", rc)
+    return out, lse
+
+
+def decode_workspace_bytes_multi(B: int, Hq: int, q_len: int, D: int, n_splits: int) -> int:
+    return int(lib().attn_decode_workspace_bytes_multi(B, Hq, q_len, D, n_splits))
+
+
+def attn_decode_splitk_multi(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens: torch.Tensor,
+                             block_table: Optional[torch.Tensor] = None, n_splits: int = 16,
+                             scale: Optional[float] = None, max_kv_len: Optional[int] = None,
+                             workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                             lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Split-K decode of q_len queries per sequence at its last positions (causal
+    among themselves: query i sees keys t <= seq_lens[b] - q_len + i).
+
+    q [B,Hq,q_len,D]; k/v and block_table as for attn_decode_splitk.
+    Returns (o [B,Hq,q_len,D], lse [B,Hq,q_len] fp32).
+    """
+    B, Hq, q_len, D = q.shape
+    Hkv, page_size, max_pages, max_kv_len = _decode_layout(k, block_table, max_kv_len)
+    _decode_checks(q, k, v, seq_lens)
+    need = decode_workspace_bytes_multi(B, Hq, q_len, D, n_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, q_len), dtype=torch.float32, device=q.device)
+    sc = default_scale(D) if scale is None else float(scale)
+    rc = lib().attn_decode_splitk_multi(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(seq_lens),
+                                        _ptr(block_table), max_pages, page_size, B, Hq, Hkv, q_len, D,
+                                        max_kv_len, sc, int(n_splits), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(),
+                                        _TORCH_DT[q.dtype], _stream(q.device))
+    _check("attn_decode_splitk_multi", rc)
     return out, lse

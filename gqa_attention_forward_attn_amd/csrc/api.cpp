@@ -74,19 +74,24 @@ gqa_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, floa
     return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 
-size_t attn_decode_workspace_bytes(int B, int Hq, int D, int n_splits) {
-    if (B <= 0 || Hq <= 0 || D <= 0 || n_splits <= 0) return 0;
-    return (size_t)B * (size_t)Hq * (size_t)n_splits * ((size_t)D + 1) * sizeof(float);
+size_t attn_decode_workspace_bytes_multi(int B, int Hq, int q_len, int D, int n_splits) {
+    if (B <= 0 || Hq <= 0 || q_len <= 0 || D <= 0 || n_splits <= 0) return 0;
+    return (size_t)B * (size_t)Hq * (size_t)q_len * (size_t)n_splits * ((size_t)D + 1) * sizeof(float);
 }
 
-gqa_status_t attn_decode_splitk(const void* q, const void* k, const void* v, void* o, float* lse,
-                                const int* seq_lens, const int* block_table,
-                                int max_pages_per_seq, int page_size,
-                                int B, int Hq, int Hkv, int D, int max_kv_len,
-                                float scale, int n_splits,
-                                void* workspace, size_t workspace_bytes,
-                                gqa_dtype_t dtype, void* hip_stream) {
+size_t attn_decode_workspace_bytes(int B, int Hq, int D, int n_splits) {
+    return attn_decode_workspace_bytes_multi(B, Hq, 1, D, n_splits);
+}
+
+gqa_status_t attn_decode_splitk_multi(const void* q, const void* k, const void* v, void* o, float* lse,
+                                      const int* seq_lens, const int* block_table,
+                                      int max_pages_per_seq, int page_size,
+                                      int B, int Hq, int Hkv, int q_len, int D, int max_kv_len,
+                                      float scale, int n_splits,
+                                      void* workspace, size_t workspace_bytes,
+                                      gqa_dtype_t dtype, void* hip_stream) {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || max_kv_len < 0) return GQA_ERR_INVALID_ARG;
+    if (q_len < 1 || q_len > 256) return GQA_ERR_INVALID_ARG;
     if (Hq % Hkv != 0) return GQA_ERR_INVALID_ARG;
     if (n_splits < 1 || n_splits > 256) return GQA_ERR_INVALID_ARG;
     if (!valid_dtype(dtype)) return GQA_ERR_INVALID_ARG;
@@ -102,7 +107,8 @@ gqa_status_t attn_decode_splitk(const void* q, const void* k, const void* v, voi
     if (B == 0) return GQA_OK;
     if (!q || !k || !v || !o || !lse || !seq_lens) return GQA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return GQA_ERR_INVALID_ARG;
-    const size_t need = attn_decode_workspace_bytes(B, Hq, D, n_splits);
+    if ((long long)B * Hq * q_len > 0x7fffffffLL) return GQA_ERR_INVALID_ARG;
+    const size_t need = attn_decode_workspace_bytes_multi(B, Hq, q_len, D, n_splits);
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return GQA_ERR_WORKSPACE;
 
     gqa::DecodeArgs a{};
@@ -110,8 +116,9 @@ gqa_status_t attn_decode_splitk(const void* q, const void* k, const void* v, voi
     a.seq_lens = seq_lens;
     a.block_table = block_table;
     a.part_o = static_cast<float*>(workspace);
-    a.part_lse = a.part_o + (size_t)B * Hq * n_splits * D;
+    a.part_lse = a.part_o + (size_t)B * Hq * q_len * n_splits * D;
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.group = Hq / Hkv;
+    a.q_len = q_len;
     a.max_pages = max_pages_per_seq;
     a.page_shift = page_shift;
     a.max_kv_len = max_kv_len;
@@ -119,6 +126,18 @@ gqa_status_t attn_decode_splitk(const void* q, const void* k, const void* v, voi
     a.c = scale * kLog2e;
     hipError_t e = gqa::launch_decode(a, to_kernel_dtype(dtype), static_cast<hipStream_t>(hip_stream));
     return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+gqa_status_t attn_decode_splitk(const void* q, const void* k, const void* v, void* o, float* lse,
+                                const int* seq_lens, const int* block_table,
+                                int max_pages_per_seq, int page_size,
+                                int B, int Hq, int Hkv, int D, int max_kv_len,
+                                float scale, int n_splits,
+                                void* workspace, size_t workspace_bytes,
+                                gqa_dtype_t dtype, void* hip_stream) {
+    return attn_decode_splitk_multi(q, k, v, o, lse, seq_lens, block_table, max_pages_per_seq, page_size,
+                                    B, Hq, Hkv, 1, D, max_kv_len, scale, n_splits, workspace,
+                                    workspace_bytes, dtype, hip_stream);
 }
 
 const char* attn_status_str(gqa_status_t s) {

@@ -10,11 +10,17 @@
 // block table, page block_table[b, t / page_size], row t % page_size (the
 // PAGE_SIZE branch of `_fwd_kernel_splitK`).
 //
+// Several queries per sequence (speculative / chunked decode, the Mq > 1 case
+// of `_fwd_kernel_splitK`): a sequence of len keys carries q_len queries at its
+// last positions, so query i sees keys t <= len - q_len + i (bottom-right
+// causal).  q_len = 1 is plain decode.
+//
 // gfx950 mapping.  Decode reads every K/V byte once, so it is bound by HBM;
 // the arithmetic still goes to the matrix cores so that the vector ALUs stay
-// nearly idle.  A workgroup owns one (sequence, K/V head, chunk) and up to 16
-// query heads of the group, which are the 16 columns of the MFMA tiles (heads
-// beyond the group are zero columns).  Each wave streams its own 16-token
+// nearly idle.  The query rows of one K/V head group, (head hh, query i) ->
+// column hh * q_len + i, are contiguous in q; a workgroup owns one (sequence,
+// K/V head, chunk) and 16 of those columns, the 16 columns of the MFMA tiles
+// (columns beyond the group are zero).  Each wave streams its own 16-token
 // slices of the chunk (wave w takes slices w, w + NW, ...):
 //
 //   K, V slice (16 rows)  --global_load_lds_dwordx4-->  per-wave LDS ring of NST stages
@@ -172,8 +178,9 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-    // ---- work item: (b, split, head block, kv head), kv head fastest -------
-    const int n_hb = (a.group + 15) >> 4;
+    // ---- work item: (b, split, column block, kv head), kv head fastest ------
+    const int ncol = a.group * a.q_len;     // query rows of the group
+    const int n_hb = (ncol + 15) >> 4;
     int id = blockIdx.x;
     const int g = id % a.Hkv;
     id /= a.Hkv;
@@ -181,8 +188,8 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
     id /= n_hb;
     const int s = id % a.n_splits;
     const int b = id / a.n_splits;
-    const int h0 = g * a.group + hb * 16;
-    const int nh = min(16, a.group - hb * 16);
+    const int nh = min(16, ncol - hb * 16);  // columns of this block
+    const size_t qrow0 = ((size_t)b * a.Hq + (size_t)g * a.group) * a.q_len + hb * 16;  // its first query row
 
     const int len = a.seq_lens[b];
     if (len <= 0) return;
@@ -267,7 +274,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
         const int nqi = (nh + RPI - 1) / RPI;
         for (int i = 0; i < nqi; ++i) {
             const int r = min(RPI * i + drow, nh - 1);
-            const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + h0 + r) * D +
+            const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (qrow0 + r) * D +
                                  (dchk ^ swz<D>(RPI * i + drow)) * 8;
             dma16(qp, __builtin_amdgcn_readfirstlane(wlds_u + i * 1024));
         }
@@ -298,6 +305,11 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
             }
         }
 
+        // causal limit of this lane's column: keys < lim are visible
+        const int qi = (hb * 16 + hrow) % a.q_len;
+        const int lim = min(hi, len - (a.q_len - 1 - qi));
+        const int lim_lo = min(hi, len - (a.q_len - 1));  // smallest limit of the block
+
         for (int k = 0; k < n_sl; ++k) {
             if (k + NST - 1 < n_sl) issue(k + NST - 1);
             wait_slices<PER_SLICE>(min(NST - 1, n_sl - 1 - k));
@@ -308,11 +320,11 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
             for (int ks = 0; ks < KS; ++ks) sc = mfma16x32(TAG(), lds16(st + koff[ks]), qop[ks], sc);
 
             const int T = T0 + stride * k;
-            if (T + kSlice > hi) {  // ragged last slice of the chunk
+            if (T + kSlice > lim_lo) {  // ragged last slice of the chunk, or keys past a query
                 const int tok = T + 4 * kq;
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    if (tok + r >= hi) sc[r] = -INFINITY;
+                    if (tok + r >= lim) sc[r] = -INFINITY;
             }
             const float lm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])) * a.c;
             if (__builtin_amdgcn_ballot_w64(lm > m + kRescaleLog2)) {
@@ -360,7 +372,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
         }
     }
     __syncthreads();
-    const size_t prow = ((size_t)b * a.Hq + h0) * a.n_splits + s;  // partial row of head h0
+    const size_t prow = qrow0 * a.n_splits + s;  // partial row of the block's first column
     for (int i = tid; i < nh * D; i += NW * 64) {
         const int h = i / D, d = i % D;
         float M = -INFINITY;
@@ -374,16 +386,18 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
             L += e * sl[w * 16 + h];
             O += e * sacc[(w * 16 + h) * D + d];
         }
+        // a column with no visible key in this chunk (a query before the chunk's
+        // keys) gives (0, -inf)
         const size_t row = prow + (size_t)h * a.n_splits;
-        a.part_o[row * D + d] = O / L;
-        if (d == 0) a.part_lse[row] = (M + fast_log2(L)) * kLn2;
+        a.part_o[row * D + d] = L > 0.f ? O / L : 0.f;
+        if (d == 0) a.part_lse[row] = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
     }
 }
 
-// One workgroup per (b, h): merge the non-empty chunks' partial results.  Wave
-// w merges the chunks s = w (mod 4) with weights relative to its own maximum
-// LSE (independent loads, eight at a time), and the four waves are merged
-// through LDS.
+// One workgroup per query row (b, h, i): merge the non-empty chunks' partial
+// results.  Wave w merges the chunks s = w (mod 4) with weights relative to its
+// own maximum LSE (independent loads, eight at a time), and the four waves are
+// merged through LDS.  Chunks with LSE = -inf (no visible key) weigh 0.
 template <class TAG, int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     constexpr int PER = D / 64;  // output dims per lane
@@ -391,8 +405,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     __shared__ float s_m[CW], s_w[CW], s_o[CW][D];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int row = blockIdx.x;  // b * Hq + h
-    const int len = a.seq_lens[row / a.Hq];
+    const int row = blockIdx.x;  // (b * Hq + h) * q_len + i
+    const int len = a.seq_lens[row / (a.Hq * a.q_len)];
     const int nv = len > 0 ? (len + chunk_tokens(len, a.n_splits) - 1) / chunk_tokens(len, a.n_splits) : 0;
     const float* pl = a.part_lse + (size_t)row * a.n_splits;
     const float* po = a.part_o + (size_t)row * a.n_splits * D + lane * PER;
@@ -408,7 +422,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     for (int i = 0; i < PER; ++i) O[i] = 0.f;
     for (int t0 = 0; t0 < nt; t0 += 64) {
         const int n = min(64, nt - t0);
-        const float w = lane < n ? fast_exp2((pl[wave + CW * (t0 + lane)] - M) * kLog2e) : 0.f;
+        const float lv = lane < n ? pl[wave + CW * (t0 + lane)] : -INFINITY;
+        const float w = lv == -INFINITY ? 0.f : fast_exp2((lv - M) * kLog2e);
         W += w;
         int t = 0;
         for (; t + 8 <= n; t += 8) {
@@ -468,14 +483,16 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 
 template <class TAG, int D, int PG>
 hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
-    const long long n_hb = (a.group + 15) / 16;
+    const long long n_hb = ((long long)a.group * a.q_len + 15) / 16;
     const long long blocks = (long long)a.B * a.Hkv * n_hb * a.n_splits;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((decode_split_kernel<TAG, D, DEC_NW, DEC_NST, PG>), dim3((unsigned)blocks),
                        dim3(DEC_NW * 64), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_combine_kernel<TAG, D>), dim3((unsigned)(a.B * a.Hq)), dim3(256), 0, stream, a);
+    const long long rows = (long long)a.B * a.Hq * a.q_len;
+    if (rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((decode_combine_kernel<TAG, D>), dim3((unsigned)rows), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -34,16 +34,17 @@ hipError_t launch_prefill(PrefillArgs a, int D, bool causal, int dtype, PrefillK
 hipError_t launch_prefill_pp(PrefillArgs a, int D, bool causal, int dtype, hipStream_t stream);
 
 struct DecodeArgs {
-    const void* q;            // [B, Hq, D]
+    const void* q;            // [B, Hq, q_len, D]
     const void* k;            // paged [pages, page_size, Hkv, D] or dense [B, Hkv, max_kv_len, D]
     const void* v;
-    void* o;                  // [B, Hq, D]
-    float* lse;               // [B, Hq]
-    const int* seq_lens;      // [B]
+    void* o;                  // [B, Hq, q_len, D]
+    float* lse;               // [B, Hq, q_len]
+    const int* seq_lens;      // [B] keys per sequence (the q_len queries are its last positions)
     const int* block_table;   // [B, max_pages] or nullptr (dense)
-    float* part_o;            // workspace [B, Hq, n_splits, D]
-    float* part_lse;          // workspace [B, Hq, n_splits]
+    float* part_o;            // workspace [B, Hq, q_len, n_splits, D]
+    float* part_lse;          // workspace [B, Hq, q_len, n_splits]
     int B, Hq, Hkv, D, group;
+    int q_len;                // queries per sequence (1: plain decode)
     int max_pages;
     int page_shift;           // log2(page_size) (paged)
     int max_kv_len;           // dense row stride in tokens

@@ -11,6 +11,10 @@
  *                       split along the keys and merged through the
  *                       per-chunk log-sum-exp (splitk_kernels.py,
  *                       `_fwd_kernel_splitK` and `_splitK_reduce`).
+ *   attn_decode_splitk_multi
+ *                       the same with q_len queries per sequence at its last
+ *                       positions, causal among themselves (the IS_CAUSAL /
+ *                       NUM_QUERIES_CAUSAL case of `_fwd_kernel_splitK`).
  *
  * What is computed, for batch b, query head h, query row i:
  *   g      = h / (Hq / Hkv)                       (query head -> K/V head)
@@ -133,6 +137,48 @@ gqa_status_t attn_decode_splitk(const void* q, const void* k, const void* v, voi
                                 float scale, int n_splits,
                                 void* workspace, size_t workspace_bytes,
                                 gqa_dtype_t dtype, void* hip_stream);
+
+/*
+ * attn_decode_workspace_bytes_multi - device workspace attn_decode_splitk_multi
+ * needs: B * Hq * q_len * n_splits * (D + 1) * 4 bytes.  Returns 0 for
+ * non-positive arguments.  attn_decode_workspace_bytes(B, Hq, D, n) equals
+ * attn_decode_workspace_bytes_multi(B, Hq, 1, D, n).
+ */
+size_t attn_decode_workspace_bytes_multi(int B, int Hq, int q_len, int D, int n_splits);
+
+/*
+ * attn_decode_splitk_multi - several queries per sequence (speculative or
+ * chunked decode), split-K.  splitk_kernels.py, `_fwd_kernel_splitK` with
+ * IS_CAUSAL and NUM_QUERIES_CAUSAL: the q_len queries of sequence b are its
+ * last q_len positions, so query i (0 <= i < q_len) sees the keys
+ *     t <= seq_lens[b] - q_len + i
+ * (query q_len - 1 sees all seq_lens[b] keys; a query placed before the first
+ * key sees none and gets o = 0, lse = -inf).
+ *
+ *   q           [B, Hq, q_len, D]   dtype    (read)
+ *   o           [B, Hq, q_len, D]   dtype    (written)
+ *   lse         [B, Hq, q_len]      float32  (written; natural log)
+ *   seq_lens, block_table, k, v, page_size, max_pages_per_seq, max_kv_len:
+ *               as for attn_decode_splitk (seq_lens[b] counts the keys of
+ *               sequence b, including those of its q_len query positions).
+ *   workspace   >= attn_decode_workspace_bytes_multi(B, Hq, q_len, D, n_splits)
+ *               bytes of device memory, 16-byte aligned, contents unspecified
+ *               before and after the call.
+ *
+ * The chunking is that of attn_decode_splitk (it depends on seq_lens[b] only);
+ * a chunk that holds no key visible to a query contributes weight 0 to it.
+ * With q_len == 1 the call is attn_decode_splitk.
+ *
+ * Requirements: those of attn_decode_splitk, and 1 <= q_len <= 256,
+ * B * Hq * q_len < 2^31.  Errors as for attn_decode_splitk.
+ */
+gqa_status_t attn_decode_splitk_multi(const void* q, const void* k, const void* v, void* o, float* lse,
+                                      const int* seq_lens, const int* block_table,
+                                      int max_pages_per_seq, int page_size,
+                                      int B, int Hq, int Hkv, int q_len, int D, int max_kv_len,
+                                      float scale, int n_splits,
+                                      void* workspace, size_t workspace_bytes,
+                                      gqa_dtype_t dtype, void* hip_stream);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* attn_status_str(gqa_status_t s);

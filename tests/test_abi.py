@@ -104,6 +104,36 @@ def test_decode_validation(L):
     assert dec(L, B=0) == OK
 
 
+def test_workspace_bytes_multi(L):
+    assert L.attn_decode_workspace_bytes_multi(16, 32, 4, 128, 16) == 16 * 32 * 4 * 16 * 129 * 4
+    assert L.attn_decode_workspace_bytes_multi(16, 32, 1, 128, 16) == L.attn_decode_workspace_bytes(16, 32, 128, 16)
+    assert L.attn_decode_workspace_bytes_multi(2, 8, 0, 128, 4) == 0
+
+
+def dec_multi(L, B=2, Hq=8, Hkv=2, q_len=4, D=128, max_kv_len=512, n_splits=4, page_size=256, max_pages=2,
+              bt=P[6], ws=P[7], ws_bytes=None, dtype=BF16, scale=0.1, q=P[0], seq=P[5]):
+    if ws_bytes is None:
+        ws_bytes = L.attn_decode_workspace_bytes_multi(B, Hq, max(q_len, 1), D, n_splits)
+    return L.attn_decode_splitk_multi(q, P[1], P[2], P[3], P[4], seq, bt, max_pages, page_size,
+                                      B, Hq, Hkv, q_len, D, max_kv_len, scale, n_splits, ws, ws_bytes,
+                                      dtype, None)
+
+
+def test_decode_multi_validation(L):
+    assert dec_multi(L, q_len=0) == INVALID
+    assert dec_multi(L, q_len=257) == INVALID
+    assert dec_multi(L, Hq=6, Hkv=4) == INVALID
+    assert dec_multi(L, n_splits=0) == INVALID
+    assert dec_multi(L, page_size=96) == INVALID
+    assert dec_multi(L, D=80) == UNSUPPORTED
+    assert dec_multi(L, dtype=F32) == UNSUPPORTED
+    assert dec_multi(L, q=None) == INVALID
+    # the workspace of one query per sequence is too small for four
+    assert dec_multi(L, ws_bytes=L.attn_decode_workspace_bytes(2, 8, 128, 4)) == WORKSPACE
+    assert dec_multi(L, ws=None) == WORKSPACE
+    assert dec_multi(L, B=0) == OK
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     q = torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16)

@@ -270,3 +270,101 @@ def test_decode_dense_matches_paged():
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
     o_ref, l_ref = oracle.attn_decode(inp.q, kd, vd, inp.seq_lens, 0.125)
     check(o2, l2, o_ref, l_ref, "f16", "dense")
+
+
+# ---- several queries per sequence ---------------------------------------------
+
+def gpu_decode_multi(inp, n_splits, scale, paged=True):
+    q = inp.q.cuda()
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device="cuda")
+    if paged:
+        o, l = gqa.attn_decode_splitk_multi(q, inp.k_cache.cuda(), inp.v_cache.cuda(), inp.seq_lens.cuda(),
+                                            block_table=inp.block_table.cuda(), n_splits=n_splits,
+                                            scale=scale, max_kv_len=inp.max_kv_len, out=out, lse=lse)
+    else:
+        o, l = gqa.attn_decode_splitk_multi(q, inp.k_dense.cuda(), inp.v_dense.cuda(), inp.seq_lens.cuda(),
+                                            n_splits=n_splits, scale=scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return o.double().cpu().numpy(), l.double().cpu().numpy()
+
+
+def oracle_multi(inp, scale, k=None, v=None, block_table="pool"):
+    if block_table == "pool":
+        return oracle.attn_decode_multi(inp.q, inp.k_cache, inp.v_cache, inp.seq_lens, scale,
+                                        block_table=inp.block_table, max_kv_len=inp.max_kv_len)
+    return oracle.attn_decode_multi(inp.q, k, v, inp.seq_lens, scale)
+
+
+def test_decode_multi_workload_all_rows():
+    spec = W.MULTI_QUERY_DECODE
+    print("workload multi_query_decode", flush=True)
+    inp = W.make_decode_spec(spec)
+    scale = W.fp32_scale(spec.D)
+    o, l = gpu_decode_multi(inp, spec.n_splits, scale)
+    o_ref, l_ref = oracle_multi(inp, scale)
+    e_o, e_l = check(o, l, o_ref, l_ref, "bf16", "multi_query_decode")
+    print(f"multi_query_decode: max|dO|={e_o:.3e} max|dLSE|={e_l:.3e}")
+
+
+DECODE_MULTI = [
+    # B, Hq, Hkv, D, dtype, q_len, len_lo, len_hi, page_size, n_splits
+    (4, 32, 8, 128, "bf16", 4, 1, 700, 256, 16),      # 4 heads x 4 queries: one block of 16 columns
+    (3, 8, 2, 128, "f16", 2, 1, 300, 16, 3),
+    (2, 16, 2, 128, "bf16", 8, 100, 2000, 64, 64),    # 8 heads x 8 queries: four column blocks
+    (5, 4, 2, 64, "f16", 16, 1, 63, 1, 1),            # page size 1; some sequences shorter than q_len
+    (2, 6, 3, 64, "bf16", 3, 500, 900, 128, 7),       # 6 columns
+    (3, 32, 4, 128, "bf16", 5, 1, 200, 16, 16),       # 40 columns: a ragged last block; many empty splits
+]
+
+
+@pytest.mark.parametrize("case", DECODE_MULTI, ids=lambda c: "-".join(map(str, c)))
+def test_decode_multi_cases(case):
+    B, Hq, Hkv, D, dt, q_len, lo, hi, ps, ns = case
+    print(f"multi-query decode case {case}", flush=True)
+    inp = W.make_decode(B, Hq, Hkv, D, dt, seed=sum(case[:4]) + hi + q_len, len_lo=lo, len_hi=hi,
+                        page_size=ps, q_len=q_len)
+    scale = W.fp32_scale(D)
+    o, l = gpu_decode_multi(inp, ns, scale)
+    o_ref, l_ref = oracle_multi(inp, scale)
+    check(o, l, o_ref, l_ref, dt, str(case))
+
+
+def test_decode_multi_short_sequences_and_invisible_chunks():
+    # len 0: nothing; len 1 and 3 with 16 queries: the leading queries see no key;
+    # len 961 with 16 splits: the last 64-token chunk holds key 960 only, which the
+    # first 15 queries do not see, so that chunk weighs 0 for them.
+    inp = W.make_decode(5, 8, 2, 128, "bf16", seed=31, seq_lens=[0, 1, 3, 961, 64], page_size=64,
+                        max_pages=16, q_len=16)
+    inp.block_table[0, 0] = 0  # never read for an empty sequence
+    o, l = gpu_decode_multi(inp, 16, 0.09)
+    o_ref, l_ref = oracle_multi(inp, 0.09)
+    check(o, l, o_ref, l_ref, "bf16", "short / invisible chunks")
+    assert np.all(o[0] == 0) and np.all(np.isneginf(l[0]))
+    assert np.all(np.isneginf(l[1, :, :15])) and np.all(np.isfinite(l[1, :, 15]))
+
+
+def test_decode_multi_single_query_equals_decode_bitwise():
+    inp = W.make_decode(3, 16, 4, 128, "bf16", seed=32, len_lo=200, len_hi=3000, page_size=256)
+    o1, l1 = gpu_decode(inp, 16, 0.088)
+    inp.q = inp.q.unsqueeze(2).contiguous()
+    o2, l2 = gpu_decode_multi(inp, 16, 0.088)
+    assert np.array_equal(o1, o2[:, :, 0]) and np.array_equal(l1, l2[:, :, 0])
+
+
+def test_decode_multi_dense_matches_paged():
+    inp = W.make_decode(3, 8, 2, 64, "f16", seed=33, len_lo=1, len_hi=500, page_size=32, q_len=6)
+    L = inp.max_kv_len
+    kd = torch.zeros(3, 2, L, 64, dtype=torch.float16)
+    vd = torch.zeros(3, 2, L, 64, dtype=torch.float16)
+    for s in range(3):
+        n = int(inp.seq_lens[s])
+        pages = inp.block_table[s, :(n + 31) // 32].long()
+        kd[s, :, :n] = inp.k_cache[pages].reshape(-1, 2, 64)[:n].permute(1, 0, 2)
+        vd[s, :, :n] = inp.v_cache[pages].reshape(-1, 2, 64)[:n].permute(1, 0, 2)
+    inp.k_dense, inp.v_dense = kd, vd
+    o1, l1 = gpu_decode_multi(inp, 4, 0.125, paged=True)
+    o2, l2 = gpu_decode_multi(inp, 4, 0.125, paged=False)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    o_ref, l_ref = oracle_multi(inp, 0.125, kd, vd, block_table=None)
+    check(o2, l2, o_ref, l_ref, "f16", "dense multi")
