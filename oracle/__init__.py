@@ -70,6 +70,9 @@ def _load():
     lib.oracle_attn_decode_multi.argtypes = [vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
                                              i32, i32, i32, f64, vp, i64, vp, vp]
     lib.oracle_attn_decode_multi.restype = i32
+    lib.oracle_attn_prefill_paged.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32,
+                                              i32, f64, i32, vp, i64, vp, vp]
+    lib.oracle_attn_prefill_paged.restype = i32
     _lib = lib
     return lib
 
@@ -253,4 +256,40 @@ def attn_decode_multi(q, k, v, seq_lens, scale: float, block_table=None, max_kv_
         raise ValueError("oracle_attn_decode_multi: bad arguments")
     if r is None:
         return o.reshape(B, Hq, q_len, D), lse.reshape(B, Hq, q_len)
+    return o, lse
+
+
+def attn_prefill_paged(q, k_cache, v_cache, qo_indptr, kv_indptr, kv_indices, scale: float,
+                       causal: bool = True, kv_last_page_len=None, rows=None):
+    """Prefill of ragged requests over a paged KV cache.
+
+    q [total_q, Hq, D] token-major; k/v_cache [num_pages, page_size, Hkv, D];
+    qo_indptr, kv_indptr [B + 1] int; kv_indices [nnz_pages] int; optional
+    kv_last_page_len [B].  Returns (o [total_q, Hq, D], lse [total_q, Hq]) or,
+    with rows, (o [n, D], lse [n]) for flat ids token*Hq + h.
+    """
+    q, k, v = _cpu(q), _cpu(k_cache), _cpu(v_cache)
+    dt = _dt(q, k, v)
+    total_q, Hq, D = q.shape
+    page_size, Hkv = k.shape[1], k.shape[2]
+    qi = _cpu(torch.as_tensor(qo_indptr), torch.int32)
+    ki = _cpu(torch.as_tensor(kv_indptr), torch.int32)
+    kx = _cpu(torch.as_tensor(kv_indices), torch.int32)
+    if kx.numel() == 0:
+        kx = torch.zeros(1, dtype=torch.int32)
+    last = None if kv_last_page_len is None else _cpu(torch.as_tensor(kv_last_page_len), torch.int32)
+    B = qi.numel() - 1
+    if int(qi[B]) != total_q:
+        raise ValueError("qo_indptr[-1] must equal q.shape[0]")
+    r = _rows(rows)
+    n = total_q * Hq if r is None else r.shape[0]
+    o = np.empty((n, D), dtype=np.float64)
+    lse = np.empty((n,), dtype=np.float64)
+    rc = _load().oracle_attn_prefill_paged(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(qi), _ptr(ki), _ptr(kx),
+                                           _ptr(last), B, Hq, Hkv, D, page_size, float(scale),
+                                           int(bool(causal)), _np_ptr(r), n, _np_ptr(o), _np_ptr(lse))
+    if rc:
+        raise ValueError("oracle_attn_prefill_paged: bad arguments")
+    if r is None:
+        return o.reshape(total_q, Hq, D), lse.reshape(total_q, Hq)
     return o, lse

@@ -335,6 +335,66 @@ int oracle_attn_decode_multi(const void* q, const void* k, const void* v, int dt
 }
 
 /*
+ * Batched prefill of ragged requests over a paged KV cache.  [P2]
+ * `_gqa_prefill_kernel` and its entry point: request b owns the query tokens
+ * [qo_indptr[b], qo_indptr[b+1]) of the token-major q [total_q, Hq, D] and the
+ * pages kv_indices[kv_indptr[b] .. kv_indptr[b+1]) of the pool
+ * [num_pages, page_size, Hkv, D] (its key t is row t % page_size of page
+ * kv_indices[kv_indptr[b] + t / page_size]).  With n_b pages, kv_len_b =
+ * (n_b - 1) * page_size + kv_last_page_len[b], or n_b * page_size when
+ * kv_last_page_len is NULL.  Query i of the request sees key t iff
+ * !causal or t <= i + kv_len_b - q_len_b ([P2] bottom-right mask).
+ *
+ * rows are flat (token * Hq + h) ids (NULL = all total_q * Hq).
+ * o_out [n_rows, D], lse_out [n_rows].  Returns 0, or 1 on a bad argument.
+ */
+int oracle_attn_prefill_paged(const void* q, const void* k, const void* v, int dt,
+                              const int* qo_indptr, const int* kv_indptr, const int* kv_indices,
+                              const int* kv_last_page_len, int B, int Hq, int Hkv, int D,
+                              int page_size, double scale, int causal,
+                              const int64_t* rows, int64_t n_rows,
+                              double* o_out, double* lse_out) {
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv || page_size <= 0) return 1;
+    const int64_t total_q = B > 0 ? qo_indptr[B] : 0;
+    const int64_t total = total_q * Hq;
+    if (!rows) n_rows = total;
+    const int group = Hq / Hkv;
+    int64_t max_kv = 1;
+    for (int b = 0; b < B; ++b) {
+        int64_t n = kv_indptr[b + 1] - kv_indptr[b];
+        if (n < 0 || qo_indptr[b + 1] < qo_indptr[b]) return 1;
+        if (n * page_size > max_kv) max_kv = n * page_size;
+    }
+    int bad = 0;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)max_kv);
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t n = 0; n < n_rows; ++n) {
+            int64_t r = rows ? rows[n] : n;
+            if (r < 0 || r >= total) { bad = 1; continue; }
+            int64_t tok = r / Hq;
+            int h = (int)(r % Hq);
+            int b = 0;
+            while (b + 1 < B && qo_indptr[b + 1] <= tok) ++b;  /* request holding the token */
+            int64_t i = tok - qo_indptr[b];
+            int64_t q_len = qo_indptr[b + 1] - qo_indptr[b];
+            int64_t n_pages = kv_indptr[b + 1] - kv_indptr[b];
+            int64_t kv_len = 0;
+            if (n_pages > 0)
+                kv_len = (n_pages - 1) * page_size + (kv_last_page_len ? kv_last_page_len[b] : page_size);
+            int g = h / group;
+            kv_view kv = {k, v, dt, D, 0, kv_indices + kv_indptr[b], page_size, Hkv, g};
+            int64_t vis_end = causal ? i + 1 + (kv_len - q_len) : kv_len;
+            attend_one(q, r * (int64_t)D, dt, &kv, 0, kv_len, vis_end, scale, s,
+                       o_out + n * (int64_t)D, lse_out + n, NULL);
+        }
+        free(s);
+    }
+    return bad;
+}
+
+/*
  * Split-K decode by the split/merge route, for the invariant tests.
  * bounds is [B, n_splits + 1]: chunk s of sequence b covers tokens
  * [bounds[b][s], bounds[b][s+1]) clipped to seq_lens[b].  Each chunk's

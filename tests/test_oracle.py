@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import oracle
-from workloads import make_prefill, make_decode, fp32_scale
+from workloads import make_prefill, make_decode, make_paged_prefill, fp32_scale
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 TOL = 1e-12
@@ -388,3 +388,53 @@ def test_decode_multi_matches_torch_reference(q_len, dtype):
         np.testing.assert_array_equal(np.isinf(l[b]), np.isinf(l_ref[0]))
         fin = np.isfinite(l_ref[0])
         np.testing.assert_allclose(l[b][fin], l_ref[0][fin], atol=TOL, rtol=0)
+
+
+# ---- ragged prefill over a paged cache ---------------------------------------
+
+def _gather_request(inp, b, Hkv, D):
+    """Dense [1, Hkv, kv_len, D] K/V of request b, gathered page by page."""
+    ps = inp.page_size
+    p0, p1 = int(inp.kv_indptr[b]), int(inp.kv_indptr[b + 1])
+    n = 0 if p1 == p0 else (p1 - p0 - 1) * ps + int(inp.kv_last_page_len[b])
+    pages = inp.kv_indices[p0:p1].long()
+    kd = inp.k_cache[pages].reshape(-1, Hkv, D)[:n].permute(1, 0, 2).unsqueeze(0).contiguous()
+    vd = inp.v_cache[pages].reshape(-1, Hkv, D)[:n].permute(1, 0, 2).unsqueeze(0).contiguous()
+    return kd, vd
+
+
+@pytest.mark.parametrize("page_size,causal,dtype", [(1, True, "f32"), (4, True, "bf16"), (8, False, "f32"),
+                                                    (16, True, "f16")])
+def test_paged_prefill_matches_torch_reference_per_request(page_size, causal, dtype):
+    # Every request against torch fp64 over its own gathered K/V; the lengths
+    # include empty requests, requests with no keys, q_len > kv_len (leading
+    # rows see nothing) and partly filled last pages.
+    q_lens = [3, 0, 5, 7, 1, 4]
+    kv_lens = [9, 4, 0, 3, 17, 4]
+    inp = make_paged_prefill(6, 8, 2, 16, dtype, seed=40 + page_size, page_size=page_size,
+                             q_lens=q_lens, kv_lens=kv_lens)
+    o, l = oracle.attn_prefill_paged(inp.q, inp.k_cache, inp.v_cache, inp.qo_indptr, inp.kv_indptr,
+                                     inp.kv_indices, 0.3, causal, inp.kv_last_page_len)
+    for b in range(6):
+        t0, t1 = int(inp.qo_indptr[b]), int(inp.qo_indptr[b + 1])
+        if t1 == t0:
+            continue
+        kd, vd = _gather_request(inp, b, 2, 16)
+        qd = inp.q[t0:t1].permute(1, 0, 2).unsqueeze(0).contiguous()   # [1, Hq, q_len, D]
+        o_ref, l_ref = torch_reference(qd, kd, vd, 0.3, causal)
+        np.testing.assert_allclose(o[t0:t1], o_ref[0].transpose(1, 0, 2), atol=TOL, rtol=0)
+        lr = l_ref[0].T
+        np.testing.assert_array_equal(np.isneginf(l[t0:t1]), np.isneginf(lr))
+        fin = np.isfinite(lr)
+        np.testing.assert_allclose(l[t0:t1][fin], lr[fin], atol=TOL, rtol=0)
+
+
+def test_paged_prefill_equals_dense_forward():
+    # One request with a full page table is the dense forward over the same K/V.
+    inp = make_paged_prefill(1, 4, 2, 32, "bf16", seed=47, page_size=8, q_lens=[13], kv_lens=[29])
+    kd, vd = _gather_request(inp, 0, 2, 32)
+    qd = inp.q.permute(1, 0, 2).unsqueeze(0).contiguous()
+    o1, l1 = oracle.attn_prefill_paged(inp.q, inp.k_cache, inp.v_cache, inp.qo_indptr, inp.kv_indptr,
+                                       inp.kv_indices, 0.2, True, inp.kv_last_page_len)
+    o2, l2 = oracle.attn_fwd(qd, kd, vd, 0.2, True)
+    assert np.array_equal(o1, o2[0].transpose(1, 0, 2)) and np.array_equal(l1, l2[0].T)

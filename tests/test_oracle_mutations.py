@@ -39,6 +39,10 @@ MUTANTS = {
                                         "int64_t vis_end = len - q_len + i;"),
     "multi_query_order_reversed": ("int64_t vis_end = len - q_len + i + 1;",
                                    "int64_t vis_end = len - i;"),
+    "paged_prefill_last_page_ignored": ("kv_len = (n_pages - 1) * page_size + (kv_last_page_len ? kv_last_page_len[b] : page_size);",
+                                        "kv_len = n_pages * page_size;"),
+    "paged_prefill_top_left": ("int64_t vis_end = causal ? i + 1 + (kv_len - q_len) : kv_len;",
+                               "int64_t vis_end = causal ? i + 1 : kv_len;"),
 }
 
 

@@ -16,6 +16,10 @@ Workloads (shapes of the attention problems the pages state):
   paged_decode          B=16 Hq=32 Hkv=8 D=128, bf16, kv_len ~ U[1024, 32768],
                         256-token pages placed by a seeded permutation, 16 splits
   multi_query_decode    the same with 4 queries per sequence at its last positions
+  ragged_paged_prefill  8 requests, Hq=32 Hkv=4 D=128, bf16, causal; request b has
+                        q_len ~ U[256, 2048] new tokens after a cached prefix of
+                        U[0, 2048] tokens; one token per page, pages placed by a
+                        seeded permutation; q token-major [total_q, Hq, D]
 """
 from __future__ import annotations
 
@@ -75,6 +79,29 @@ MULTI_QUERY_DECODE = DecodeSpec("multi_query_decode", 16, 32, 8, 128, "bf16", 10
                                 20266, q_len=4)
 
 PREFILL_WORKLOADS = [CAUSAL_GQA_FP32, CAUSAL_GQA_PREFILL, CAUSAL_GQA_OFFSET, MHA_NONCAUSAL_FP16]
+
+
+@dataclass(frozen=True)
+class PagedPrefillSpec:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    dtype: str
+    q_lo: int            # new query tokens per request ~ U[q_lo, q_hi]
+    q_hi: int
+    prefix_lo: int       # cached tokens before them ~ U[prefix_lo, prefix_hi]
+    prefix_hi: int
+    page_size: int
+    causal: bool
+    seed: int
+
+
+# Batched prefill over a paged cache with the head geometry of the FlashInfer-style
+# prefill page (32 query heads, 4 K/V heads, D = 128, one token per page).
+RAGGED_PAGED_PREFILL = PagedPrefillSpec("ragged_paged_prefill", 8, 32, 4, 128, "bf16", 256, 2048, 0, 2048,
+                                        1, True, 20267)
 
 
 def _randn(shape, g, dtype, mult=1.0):
@@ -146,3 +173,57 @@ def make_decode_spec(spec: DecodeSpec):
                        spec.len_lo, spec.len_hi, spec.page_size, spec.max_pages,
                        q_len=None if spec.q_len == 1 else spec.q_len)
 
+
+
+@dataclass
+class PagedPrefillInputs:
+    q: torch.Tensor                  # [total_q, Hq, D]
+    k_cache: torch.Tensor            # [num_pages, page_size, Hkv, D]
+    v_cache: torch.Tensor
+    qo_indptr: torch.Tensor          # [B + 1] int32
+    kv_indptr: torch.Tensor          # [B + 1] int32 (page offsets into kv_indices)
+    kv_indices: torch.Tensor         # [nnz_pages] int32
+    kv_last_page_len: torch.Tensor   # [B] int32 (tokens in each request's last page)
+    page_size: int
+    max_q_len: int
+
+
+def make_paged_prefill(B, Hq, Hkv, D, dtype="bf16", seed=0, q_lo=1, q_hi=64, prefix_lo=0, prefix_hi=64,
+                       page_size=16, q_lens=None, kv_lens=None, permute=True):
+    """Ragged prefill inputs over a paged pool, drawn in the order q_lens,
+    prefix lengths, q, page permutation, K, V (q_lens / kv_lens may be given).
+
+    Request b has q_lens[b] new tokens and kv_lens[b] keys (its cached prefix
+    and its own tokens, kv_len = prefix + q_len by default); its
+    ceil(kv_len / page_size) pages are handed out from a seeded permutation of
+    all pages in request order.
+    """
+    g = torch.Generator().manual_seed(seed)
+    dt = _DTYPES[dtype]
+    if q_lens is None:
+        q_lens = torch.randint(q_lo, q_hi + 1, (B,), generator=g, dtype=torch.int64)
+    q_lens = torch.as_tensor(q_lens, dtype=torch.int64)
+    if kv_lens is None:
+        prefix = torch.randint(prefix_lo, prefix_hi + 1, (B,), generator=g, dtype=torch.int64)
+        kv_lens = q_lens + prefix
+    kv_lens = torch.as_tensor(kv_lens, dtype=torch.int64)
+    total_q = int(q_lens.sum())
+    q = _randn((total_q, Hq, D), g, dt)
+    n_pages = [(int(n) + page_size - 1) // page_size for n in kv_lens]
+    total_pages = max(1, sum(n_pages))
+    perm = torch.randperm(total_pages, generator=g) if permute else torch.arange(total_pages)
+    k = _randn((total_pages, page_size, Hkv, D), g, dt)
+    v = _randn((total_pages, page_size, Hkv, D), g, dt)
+    qo = torch.zeros(B + 1, dtype=torch.int32)
+    qo[1:] = torch.cumsum(q_lens, 0).to(torch.int32)
+    kvp = torch.zeros(B + 1, dtype=torch.int32)
+    kvp[1:] = torch.cumsum(torch.as_tensor(n_pages, dtype=torch.int64), 0).to(torch.int32)
+    idx = perm[:sum(n_pages)].to(torch.int32)
+    last = torch.tensor([int(n) - (p - 1) * page_size if p > 0 else 0 for n, p in zip(kv_lens, n_pages)],
+                        dtype=torch.int32)
+    return PagedPrefillInputs(q, k, v, qo, kvp, idx, last, page_size, max(1, int(q_lens.max()) if B else 1))
+
+
+def make_paged_prefill_spec(spec: PagedPrefillSpec):
+    return make_paged_prefill(spec.B, spec.Hq, spec.Hkv, spec.D, spec.dtype, spec.seed, spec.q_lo, spec.q_hi,
+                              spec.prefix_lo, spec.prefix_hi, spec.page_size)
