@@ -5,8 +5,9 @@ Prints ONE JSON line.  The headline workload is causal GQA prefill in bf16
 batch, inputs already resident in HBM.  `value` is TFLOP/s counted on the
 visible (query, key) pairs only (4*D flop per pair; masked work is not
 credited).  The other workloads (fp32 correctness shape, bottom-right offset
-prefill, non-causal fp16 MHA, split-K paged decode) are timed the same way and
-reported under "workloads".
+prefill, non-causal fp16 MHA, split-K paged decode with one and with four
+queries per sequence, ragged prefill over a paged cache) are timed the same way
+and reported under "workloads".
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--only NAME]
 """
@@ -148,6 +149,41 @@ def bench_prefill(spec, steps, warmup):
 COPY_BYTES = 512 << 20
 
 
+def bench_paged_prefill(spec, steps, warmup):
+    inp = W.make_paged_prefill_spec(spec)
+    dev = torch.device("cuda:0")
+    q = inp.q.to(dev)
+    kc, vc = inp.k_cache.to(dev), inp.v_cache.to(dev)
+    qo, kvp, idx, last = (t.to(dev) for t in (inp.qo_indptr, inp.kv_indptr, inp.kv_indices,
+                                                 inp.kv_last_page_len))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    scale = W.fp32_scale(spec.D)
+
+    def step():
+        gqa.attn_prefill_paged(q, kc, vc, qo, kvp, idx, inp.max_q_len, kv_last_page_len=last,
+                               causal=spec.causal, scale=scale, out=o, lse=lse)
+
+    wall, kern_s, per = time_launches(step, steps, warmup)
+    q_lens = (inp.qo_indptr[1:] - inp.qo_indptr[:-1]).tolist()
+    n_pages = (inp.kv_indptr[1:] - inp.kv_indptr[:-1]).tolist()
+    kv_lens = [0 if n == 0 else (n - 1) * spec.page_size + int(lp)
+               for n, lp in zip(n_pages, inp.kv_last_page_len.tolist())]
+    flops = 4 * spec.D * spec.Hq * sum(visible_pairs(a, b, spec.causal) for a, b in zip(q_lens, kv_lens))
+    return {
+        "workload": spec.name, "dtype": spec.dtype, "causal": spec.causal,
+        "shape": {"B": spec.B, "Hq": spec.Hq, "Hkv": spec.Hkv, "D": spec.D, "page_size": spec.page_size,
+                  "total_q": int(sum(q_lens)), "sum_kv_len": int(sum(kv_lens))},
+        "flop_per_launch": flops,
+        "ms_per_step": wall / steps * 1e3,
+        "kernel_ms_mean": kern_s * 1e3, "kernel_ms_min": float(per.min()) * 1e3,
+        "tflops": flops * steps / wall / 1e12,
+        "kernel_tflops": flops / kern_s / 1e12,
+        "peak_tflops": PEAK_MFMA_16BIT_TFLOPS,
+        "frac_of_peak": flops / kern_s / 1e12 / PEAK_MFMA_16BIT_TFLOPS,
+    }
+
+
 def bench_copy(steps, warmup):
     """Calibration for the hardware byte counters: a plain device-to-device copy
     of COPY_BYTES (read COPY_BYTES, write COPY_BYTES) per call."""
@@ -225,6 +261,14 @@ def cpu_baseline(spec, target_s=12.0):
     }
 
 
+def run_one(spec, steps, warmup):
+    if isinstance(spec, W.DecodeSpec):
+        return bench_decode(spec, steps, warmup)
+    if isinstance(spec, W.PagedPrefillSpec):
+        return bench_paged_prefill(spec, steps, warmup)
+    return bench_prefill(spec, steps, warmup)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -245,7 +289,7 @@ def main():
         sys.exit(2)
 
     all_specs = [W.CAUSAL_GQA_FP32, W.CAUSAL_GQA_PREFILL, W.CAUSAL_GQA_OFFSET,
-                 W.MHA_NONCAUSAL_FP16, W.PAGED_DECODE, W.MULTI_QUERY_DECODE]
+                 W.MHA_NONCAUSAL_FP16, W.PAGED_DECODE, W.MULTI_QUERY_DECODE, W.RAGGED_PAGED_PREFILL]
     if args.only == "hbm_copy":
         print(json.dumps(bench_copy(args.steps, args.warmup)), flush=True)
         return
@@ -254,17 +298,14 @@ def main():
         if not specs:
             sys.exit(f"unknown workload {args.only}")
         for s in specs:
-            r = bench_decode(s, args.steps, args.warmup) if isinstance(s, W.DecodeSpec) else \
-                bench_prefill(s, args.steps, args.warmup)
-            print(json.dumps(r), flush=True)
+            print(json.dumps(run_one(s, args.steps, args.warmup)), flush=True)
         return
 
     results = {}
     for s in all_specs:
         if s is PRIMARY:
             continue
-        r = bench_decode(s, max(20, args.steps // 2), args.warmup) if isinstance(s, W.DecodeSpec) else \
-            bench_prefill(s, max(20, args.steps // 2), args.warmup)
+        r = run_one(s, max(20, args.steps // 2), args.warmup)
         results[s.name] = r
         print(f"# {s.name}: {json.dumps(r)}", file=sys.stderr, flush=True)
 

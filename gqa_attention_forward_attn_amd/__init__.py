@@ -23,7 +23,7 @@ STATUS = {0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_UNSUPPORTED",
 _TORCH_DT = {torch.float32: GQA_F32, torch.float16: GQA_F16, torch.bfloat16: GQA_BF16}
 
 # Every symbol include/gqa_attn.h declares.
-EXPORTS = ("attn_fwd", "attn_decode_workspace_bytes", "attn_decode_splitk",
+EXPORTS = ("attn_fwd", "attn_prefill_paged", "attn_decode_workspace_bytes", "attn_decode_splitk",
            "attn_decode_workspace_bytes_multi", "attn_decode_splitk_multi", "attn_status_str")
 
 _lib = None
@@ -47,6 +47,9 @@ def lib() -> ctypes.CDLL:
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32, vp]
     L.attn_fwd.restype = i32
+    L.attn_prefill_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                     f32, i32, i32, vp]
+    L.attn_prefill_paged.restype = i32
     L.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
     L.attn_decode_workspace_bytes.restype = sz
     L.attn_decode_splitk.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
@@ -105,6 +108,41 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = T
     rc = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, q_len, kv_len, D,
                         sc, int(bool(causal)), _TORCH_DT[q.dtype], _stream(q.device))
     _check("attn_fwd", rc)
+    return out, lse
+
+
+def attn_prefill_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                       qo_indptr: torch.Tensor, kv_indptr: torch.Tensor, kv_indices: torch.Tensor,
+                       max_q_len: int, kv_last_page_len: Optional[torch.Tensor] = None, causal: bool = True,
+                       scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                       lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Prefill of a batch of ragged requests over a paged KV cache.
+
+    q [total_q, Hq, D] token-major; k/v_cache [num_pages, page_size, Hkv, D];
+    qo_indptr, kv_indptr [B+1] int32; kv_indices int32 page ids; optional
+    kv_last_page_len [B] int32.  `max_q_len` (a host int) must bound every
+    request's query count.  Returns (o [total_q, Hq, D], lse [total_q, Hq] fp32).
+    """
+    total_q, Hq, D = q.shape
+    _, page_size, Hkv, Dk = k_cache.shape
+    if Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("shape mismatch between q and the K/V pool")
+    if q.dtype not in _TORCH_DT or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and the K/V pool must share one dtype")
+    for t in (qo_indptr, kv_indptr, kv_indices) + (() if kv_last_page_len is None else (kv_last_page_len,)):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise TypeError("index arrays must be contiguous int32 tensors")
+    B = qo_indptr.numel() - 1
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((total_q, Hq), dtype=torch.float32, device=q.device)
+    sc = default_scale(D) if scale is None else float(scale)
+    rc = lib().attn_prefill_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), _ptr(qo_indptr),
+                                  _ptr(kv_indptr), _ptr(kv_indices), _ptr(kv_last_page_len), B, Hq, Hkv, D,
+                                  page_size, int(max_q_len), sc, int(bool(causal)), _TORCH_DT[q.dtype],
+                                  _stream(q.device))
+    _check("attn_prefill_paged", rc)
     return out, lse
 
 

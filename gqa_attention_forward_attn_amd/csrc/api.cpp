@@ -74,6 +74,41 @@ gqa_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, floa
     return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 
+gqa_status_t attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                                const int* qo_indptr, const int* kv_indptr, const int* kv_indices,
+                                const int* kv_last_page_len, int B, int Hq, int Hkv, int D, int page_size,
+                                int max_q_len, float scale, int causal, gqa_dtype_t dtype, void* hip_stream) {
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || max_q_len < 0) return GQA_ERR_INVALID_ARG;
+    if (Hq % Hkv != 0) return GQA_ERR_INVALID_ARG;
+    if (page_size <= 0 || (page_size & (page_size - 1)) != 0) return GQA_ERR_INVALID_ARG;
+    if (!valid_dtype(dtype)) return GQA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return GQA_ERR_INVALID_ARG;
+    if (!supported_head_dim(D) || dtype == GQA_F32) return GQA_ERR_UNSUPPORTED;
+    if (B == 0 || max_q_len == 0) return GQA_OK;
+    if (!q || !k_cache || !v_cache || !o || !lse || !qo_indptr || !kv_indptr || !kv_indices)
+        return GQA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(o) || !aligned16(k_cache) || !aligned16(v_cache)) return GQA_ERR_INVALID_ARG;
+    int page_shift = 0;
+    while ((1 << page_shift) < page_size) ++page_shift;
+
+    gqa::PrefillArgs a{};
+    a.q = q; a.k = k_cache; a.v = v_cache; a.o = o; a.lse = lse;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv;
+    a.q_len = max_q_len;  // sizes the grid; each request's own lengths come from the pointers
+    a.kv_len = 0;
+    a.group = Hq / Hkv;
+    a.delta = 0;
+    a.c = scale * kLog2e;
+    a.qo_indptr = qo_indptr;
+    a.kv_indptr = kv_indptr;
+    a.kv_indices = kv_indices;
+    a.kv_last_page_len = kv_last_page_len;
+    a.page_shift = page_shift;
+    hipError_t e = gqa::launch_prefill_paged(a, D, causal != 0, to_kernel_dtype(dtype),
+                                             static_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
 size_t attn_decode_workspace_bytes_multi(int B, int Hq, int q_len, int D, int n_splits) {
     if (B <= 0 || Hq <= 0 || q_len <= 0 || D <= 0 || n_splits <= 0) return 0;
     return (size_t)B * (size_t)Hq * (size_t)q_len * (size_t)n_splits * ((size_t)D + 1) * sizeof(float);

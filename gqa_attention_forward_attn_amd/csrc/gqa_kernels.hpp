@@ -23,6 +23,14 @@ struct PrefillArgs {
     int n_pos_tiles;  // filled by the launcher
     int n_rest;       // filled by the launcher
     float c;          // scale * log2(e)
+    // Ragged batch over a paged cache (paged prefill only): q, o token-major
+    // [total_q, Hq, D], lse [total_q, Hq]; k, v [num_pages, page_size, Hkv, D].
+    // q_len holds the largest per-request query count (sizes the grid).
+    const int* qo_indptr;         // [B + 1]
+    const int* kv_indptr;         // [B + 1] offsets into kv_indices
+    const int* kv_indices;        // page ids
+    const int* kv_last_page_len;  // [B] tokens in each last page, or nullptr (full pages)
+    int page_shift;               // log2(page_size)
 };
 
 // bf16 / fp16 prefill kernel: chosen by shape, or forced (tests).
@@ -30,6 +38,8 @@ enum class PrefillKernel { kAuto, kPingPong, kFourWave };
 
 // Validated arguments only.  D in {64, 128}; dtype one of kDtype*.
 hipError_t launch_prefill(PrefillArgs a, int D, bool causal, int dtype, PrefillKernel kernel, hipStream_t stream);
+// Ragged batch of requests over a paged K/V cache (bf16 / fp16, four-wave kernel).
+hipError_t launch_prefill_paged(PrefillArgs a, int D, bool causal, int dtype, hipStream_t stream);
 // Ping-pong schedule, 8 waves x 32 rows (bf16 / fp16 only).
 hipError_t launch_prefill_pp(PrefillArgs a, int D, bool causal, int dtype, hipStream_t stream);
 

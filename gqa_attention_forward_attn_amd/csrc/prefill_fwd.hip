@@ -26,6 +26,14 @@
 //     that the A operand of each 16-key step is one 16-byte LDS read;
 //   * K/V tiles are double buffered in LDS: the global loads of tile t+1 are in
 //     flight while tile t is multiplied, one barrier per tile.
+//
+// PAGED: a batch of ragged requests over a paged K/V cache, the FlashInfer-style
+// prefill page's `run` (gpt-o3 / triton6fd1ef): request b owns the query tokens
+// [qo_indptr[b], qo_indptr[b+1]) of a token-major q [total_q, Hq, D] and the
+// pages kv_indices[kv_indptr[b] ..) of a pool [num_pages, page_size, Hkv, D];
+// its key t is row t % page_size of page kv_indices[kv_indptr[b] + t / page_size]
+// and the bottom-right offset is per request.  The page ids of a tile's rows are
+// loaded one tile ahead of its K/V loads, so the lookup adds no latency.
 #include "gqa_device.hpp"
 #include "gqa_kernels.hpp"
 
@@ -36,7 +44,7 @@ namespace {
 // Growth of a row max (log2 units) that triggers a rescale of acc and l.
 constexpr float kRescaleLog2 = 8.f;
 
-template <class TAG, int D, bool CAUSAL, int NH>
+template <class TAG, int D, bool CAUSAL, int NH, bool PAGED>
 __global__ __launch_bounds__(256, 2) void prefill_fwd_mfma(PrefillArgs a) {
     constexpr int BN = 64;                 // keys per tile
     constexpr int WPH = 4 / NH;            // waves per head
@@ -73,37 +81,62 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_mfma(PrefillArgs a) {
     const int pos0 = wg_pos0 + (wave % WPH) * 32;
     const int my_q = pos0 + l32;
 
+    // ---- the request: query rows, keys, causal offset ------------------------
+    int q_len = a.q_len, kv_len = a.kv_len, delta = a.delta;
+    size_t q_tok0 = 0;   // PAGED: first query token of the request
+    int kv_page0 = 0;    // PAGED: first entry of its page list
+    if constexpr (PAGED) {
+        q_tok0 = (size_t)a.qo_indptr[b];
+        q_len = a.qo_indptr[b + 1] - (int)q_tok0;
+        kv_page0 = a.kv_indptr[b];
+        const int n_pages = a.kv_indptr[b + 1] - kv_page0;
+        kv_len = n_pages > 0 ? ((n_pages - 1) << a.page_shift) +
+                                   (a.kv_last_page_len ? a.kv_last_page_len[b] : (1 << a.page_shift))
+                             : 0;
+        delta = kv_len - q_len;
+        if (wg_pos0 >= q_len) return;  // workgroup-uniform: past this request's queries
+    }
+    // element offset of query row `row` of head h (q and o), and its LSE index
+    auto q_off = [&](int row) -> size_t {
+        if constexpr (PAGED) return ((q_tok0 + row) * a.Hq + h) * (size_t)D;
+        return (((size_t)b * a.Hq + h) * (size_t)q_len + row) * D;
+    };
+    auto lse_off = [&](int row) -> size_t {
+        if constexpr (PAGED) return (q_tok0 + row) * a.Hq + h;
+        return ((size_t)b * a.Hq + h) * (size_t)q_len + row;
+    };
+
     // ---- key ranges -------------------------------------------------------
     // wg_kv_end: keys any row of the workgroup sees; wave_kv_end: keys any row
     // of this wave sees; wave_full_end: keys every row of this wave sees.
-    int wg_kv_end = a.kv_len, wave_kv_end = a.kv_len, wave_full_end = a.kv_len;
+    int wg_kv_end = kv_len, wave_kv_end = kv_len, wave_full_end = kv_len;
     if (CAUSAL) {
-        const int wg_last = min(wg_pos0 + POS, a.q_len) - 1;
-        wg_kv_end = max(0, min(a.kv_len, wg_last + a.delta + 1));
-        const int w_last = min(pos0 + 32, a.q_len) - 1;
-        wave_kv_end = pos0 < a.q_len ? max(0, min(a.kv_len, w_last + a.delta + 1)) : 0;
-        wave_full_end = max(0, min(a.kv_len, pos0 + a.delta + 1));
-    } else if (pos0 >= a.q_len) {
+        const int wg_last = min(wg_pos0 + POS, q_len) - 1;
+        wg_kv_end = max(0, min(kv_len, wg_last + delta + 1));
+        const int w_last = min(pos0 + 32, q_len) - 1;
+        wave_kv_end = pos0 < q_len ? max(0, min(kv_len, w_last + delta + 1)) : 0;
+        wave_full_end = max(0, min(kv_len, pos0 + delta + 1));
+    } else if (pos0 >= q_len) {
         wave_kv_end = 0;
     }
     const int n_tiles = (wg_kv_end + BN - 1) / BN;
 
     // ---- Q: B operand of S^T = K Q^T, resident in registers ---------------
-    const size_t q_head = ((size_t)b * a.Hq + h) * (size_t)a.q_len;
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + q_head * D;
-    const int q_row = min(my_q, a.q_len - 1);
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q);
+    const int q_row = min(my_q, q_len - 1);
     vec8 qf[DS];
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds)
-        qf[ds] = __builtin_bit_cast(vec8, ld_global_16(qp + (size_t)q_row * D + ds * 16 + half * 8));
+        qf[ds] = __builtin_bit_cast(vec8, ld_global_16(qp + q_off(q_row) + ds * 16 + half * 8));
     // Q must be resident before the loop: otherwise the wait-count pass makes
     // every use of Q inside the loop wait for the next tile's prefetch loads.
     wait_vmcnt0();
 
-    const size_t kv_head = ((size_t)b * a.Hkv + g) * (size_t)a.kv_len;
+    // dense: the (b, g) plane; PAGED: head g inside the pool's token rows
+    const size_t kv_head = PAGED ? (size_t)g : ((size_t)b * a.Hkv + g) * (size_t)kv_len;
     const uint16_t* kp = static_cast<const uint16_t*>(a.k) + kv_head * D;
     const uint16_t* vp = static_cast<const uint16_t*>(a.v) + kv_head * D;
-    const int last_key = a.kv_len - 1;
+    const int last_key = kv_len - 1;
 
     // ---- tile staging ------------------------------------------------------
     u32x4 kreg[KCH];
@@ -115,19 +148,41 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_mfma(PrefillArgs a) {
     // lane half feeds to a 16-key MFMA step are contiguous.
     const int v_pos = (v_kg >> 2) * 16 + 8 * (v_kg & 1) + 4 * ((v_kg >> 1) & 1);
 
+    // Element offset of key `key` (clamped to the last key) in its K/V plane;
+    // PAGED: the key's pool row from the page id fetched for it beforehand.
+    const int page_mask = PAGED ? (1 << a.page_shift) - 1 : 0;
+    const size_t tok_stride = PAGED ? (size_t)a.Hkv * D : (size_t)D;
+    auto key_row = [&](int key, int page) -> size_t {
+        if constexpr (PAGED) return (((size_t)page << a.page_shift) + (size_t)(key & page_mask)) * tok_stride;
+        return (size_t)key * D;
+    };
+    int pg_k[KCH], pg_v[4];  // PAGED: page ids of the rows of the next tile to load
+    auto fetch_pages = [&](int t0) {
+        if constexpr (PAGED) {
+            const int* ix = a.kv_indices + kv_page0;
+#pragma unroll
+            for (int j = 0; j < KCH; ++j) {
+                const int row = (tid + 256 * j) / (D / 8);
+                pg_k[j] = ix[min(t0 + row, last_key) >> a.page_shift];
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                pg_v[r] = tid < VTHREADS ? ix[min(t0 + 4 * v_kg + r, last_key) >> a.page_shift] : 0;
+        }
+    };
     auto load_tile = [&](int t0) {
 #pragma unroll
         for (int j = 0; j < KCH; ++j) {
             const int c = tid + 256 * j;
             const int row = c / (D / 8), col = c % (D / 8);
             const int key = min(t0 + row, last_key);
-            kreg[j] = ld_global_16(kp + (size_t)key * D + col * 8);
+            kreg[j] = ld_global_16(kp + key_row(key, pg_k[j]) + col * 8);
         }
         if (tid < VTHREADS) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int key = min(t0 + 4 * v_kg + r, last_key);
-                vreg[r] = ld_global_16(vp + (size_t)key * D + v_dg * 8);
+                vreg[r] = ld_global_16(vp + key_row(key, pg_v[r]) + v_dg * 8);
             }
         }
     };
@@ -161,7 +216,9 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_mfma(PrefillArgs a) {
         for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
 
     if (n_tiles > 0) {
+        fetch_pages(0);
         load_tile(0);
+        if (n_tiles > 1) fetch_pages(BN);
         store_tile(0);
     }
     __syncthreads();
@@ -170,6 +227,7 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_mfma(PrefillArgs a) {
         const int t0 = it * BN;
         const int buf = it & 1;
         if (it + 1 < n_tiles) load_tile(t0 + BN);
+        if (it + 2 < n_tiles) fetch_pages(t0 + 2 * BN);
 
         if (t0 < wave_kv_end) {  // wave-uniform: skip tiles this wave cannot see
             const uint16_t* ks = smem + buf * (KT + VT);
@@ -192,7 +250,7 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_mfma(PrefillArgs a) {
             }
 
             if (t0 + BN > wave_full_end) {  // diagonal or tail tile: apply the mask
-                const int lim = CAUSAL ? min(my_q + a.delta + 1, a.kv_len) : a.kv_len;
+                const int lim = CAUSAL ? min(my_q + delta + 1, kv_len) : kv_len;
 #pragma unroll
                 for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
@@ -257,9 +315,9 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_mfma(PrefillArgs a) {
 
     // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2 -------------------
     const float l_tot = l + xor32(l);
-    if (my_q < a.q_len) {
+    if (my_q < q_len) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        uint16_t* op = static_cast<uint16_t*>(a.o) + (q_head + my_q) * D;
+        uint16_t* op = static_cast<uint16_t*>(a.o) + q_off(my_q);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -270,7 +328,7 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_mfma(PrefillArgs a) {
                 *reinterpret_cast<u32x2*>(op + d0) = w;
             }
         if (half == 0)
-            a.lse[q_head + my_q] = l_tot > 0.f ? (m + fast_log2(l_tot)) * kLn2 : -INFINITY;
+            a.lse[lse_off(my_q)] = l_tot > 0.f ? (m + fast_log2(l_tot)) * kLn2 : -INFINITY;
     }
 }
 
@@ -448,23 +506,23 @@ __global__ __launch_bounds__(256) void prefill_fwd_f32(PrefillArgs a) {
     }
 }
 
-template <class TAG, int D, bool CAUSAL, int NH>
+template <class TAG, int D, bool CAUSAL, int NH, bool PAGED>
 hipError_t launch_mfma(PrefillArgs a, hipStream_t stream) {
     constexpr int POS = 32 * (4 / NH);
     a.n_pos_tiles = (a.q_len + POS - 1) / POS;
     a.n_rest = a.B * a.Hkv * (a.group / NH);
     const long long blocks = (long long)a.n_pos_tiles * a.n_rest;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((prefill_fwd_mfma<TAG, D, CAUSAL, NH>), dim3((unsigned)blocks), dim3(256), 0,
+    hipLaunchKernelGGL((prefill_fwd_mfma<TAG, D, CAUSAL, NH, PAGED>), dim3((unsigned)blocks), dim3(256), 0,
                        stream, a);
     return hipGetLastError();
 }
 
-template <class TAG, int D, bool CAUSAL>
+template <class TAG, int D, bool CAUSAL, bool PAGED = false>
 hipError_t dispatch_nh(PrefillArgs a, hipStream_t stream) {
-    if (a.group % 4 == 0) return launch_mfma<TAG, D, CAUSAL, 4>(a, stream);
-    if (a.group % 2 == 0) return launch_mfma<TAG, D, CAUSAL, 2>(a, stream);
-    return launch_mfma<TAG, D, CAUSAL, 1>(a, stream);
+    if (a.group % 4 == 0) return launch_mfma<TAG, D, CAUSAL, 4, PAGED>(a, stream);
+    if (a.group % 2 == 0) return launch_mfma<TAG, D, CAUSAL, 2, PAGED>(a, stream);
+    return launch_mfma<TAG, D, CAUSAL, 1, PAGED>(a, stream);
 }
 
 template <int D, bool CAUSAL>
@@ -483,7 +541,19 @@ hipError_t dispatch_d(PrefillArgs a, int D, bool causal, hipStream_t stream) {
     return causal ? dispatch_nh<TAG, 128, true>(a, stream) : dispatch_nh<TAG, 128, false>(a, stream);
 }
 
+template <class TAG>
+hipError_t dispatch_d_paged(PrefillArgs a, int D, bool causal, hipStream_t stream) {
+    if (D == 64)
+        return causal ? dispatch_nh<TAG, 64, true, true>(a, stream) : dispatch_nh<TAG, 64, false, true>(a, stream);
+    return causal ? dispatch_nh<TAG, 128, true, true>(a, stream) : dispatch_nh<TAG, 128, false, true>(a, stream);
+}
+
 }  // namespace
+
+hipError_t launch_prefill_paged(PrefillArgs a, int D, bool causal, int dtype, hipStream_t stream) {
+    if (dtype == kDtypeBF16) return dispatch_d_paged<bf16_tag>(a, D, causal, stream);
+    return dispatch_d_paged<f16_tag>(a, D, causal, stream);
+}
 
 hipError_t launch_prefill(PrefillArgs a, int D, bool causal, int dtype, PrefillKernel kernel, hipStream_t stream) {
     if (dtype != kDtypeF32 && kernel == PrefillKernel::kAuto) {

@@ -7,6 +7,10 @@
  *   attn_fwd            prefill / general forward, FlashAttention style
  *                       (causal_forward_kernel.py, `_flash_attention_forward_gqa_kernel`
  *                       and its wrapper `flash_attention_forward`).
+ *   attn_prefill_paged  the same forward for a batch of ragged requests whose
+ *                       keys live in a paged KV cache (the FlashInfer-style
+ *                       prefill page gpt-o3 / triton6fd1ef, `run` and
+ *                       `_gqa_prefill_kernel`).
  *   attn_decode_splitk  one query per sequence against a (paged) KV cache,
  *                       split along the keys and merged through the
  *                       per-chunk log-sum-exp (splitk_kernels.py,
@@ -88,6 +92,46 @@ typedef enum {
 gqa_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                       int B, int Hq, int Hkv, int q_len, int kv_len, int D,
                       float scale, int causal, gqa_dtype_t dtype, void* hip_stream);
+
+/*
+ * attn_prefill_paged - attention forward for a batch of B ragged requests over
+ * a paged KV cache (the FlashInfer-style prefill page, `run`: query tokens
+ * located by qo_indptr, key pages by kv_indptr / kv_indices).
+ *
+ *   q         [total_q, Hq, D]  dtype  (read; token-major, total_q = qo_indptr[B])
+ *   o         [total_q, Hq, D]  dtype  (written)
+ *   lse       [total_q, Hq]     float32 (written; natural log)
+ *   k_cache, v_cache [num_pages, page_size, Hkv, D] dtype (read)
+ *   qo_indptr [B + 1] int32: request b owns query tokens [qo_indptr[b], qo_indptr[b+1])
+ *   kv_indptr [B + 1] int32: request b owns the page ids
+ *             kv_indices[kv_indptr[b] .. kv_indptr[b+1]) (n_b pages, in key order)
+ *   kv_indices [kv_indptr[B]] int32: page ids into the pool
+ *   kv_last_page_len [B] int32 or NULL: keys in request b's last page
+ *             (1..page_size); NULL means every page is full.  Request b has
+ *             kv_len_b = (n_b - 1) * page_size + kv_last_page_len[b] keys
+ *             (0 when n_b = 0); its key t is row t % page_size of page
+ *             kv_indices[kv_indptr[b] + t / page_size].
+ *   max_q_len  an upper bound of every request's query count (host value; it
+ *             sizes the launch; rows of a longer request would not be computed).
+ *
+ * Query i of request b sees key t iff !causal or t <= i + kv_len_b - q_len_b
+ * (bottom-right per request, as the page's mask kv_allowed = q_idx + 1 + delta);
+ * a query with no visible key, and every query of a request without keys, gets
+ * o = 0, lse = -inf.  Requests with no queries produce nothing.
+ *
+ * The contents of the three pointer arrays and of kv_last_page_len are trusted
+ * (not bounds-checked on the device); an inconsistent table is undefined
+ * behaviour.
+ *
+ * Requirements: B >= 0, Hq, Hkv > 0, Hq % Hkv == 0, D in {64, 128}, dtype F16
+ * or BF16, page_size a power of two, max_q_len >= 0, scale finite and > 0.
+ * B == 0 or max_q_len == 0 returns GQA_OK without launching.
+ * Returns GQA_ERR_INVALID_ARG / GQA_ERR_UNSUPPORTED / GQA_ERR_HIP or GQA_OK.
+ */
+gqa_status_t attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                                const int* qo_indptr, const int* kv_indptr, const int* kv_indices,
+                                const int* kv_last_page_len, int B, int Hq, int Hkv, int D, int page_size,
+                                int max_q_len, float scale, int causal, gqa_dtype_t dtype, void* hip_stream);
 
 /*
  * attn_decode_workspace_bytes - device workspace attn_decode_splitk needs:

@@ -134,6 +134,29 @@ def test_decode_multi_validation(L):
     assert dec_multi(L, B=0) == OK
 
 
+def pre_paged(L, B=2, Hq=8, Hkv=2, D=128, page_size=16, max_q_len=64, scale=0.1, causal=1, dtype=BF16,
+              q=P[0], qo=P[5], kvp=P[6], idx=P[7], last=None):
+    return L.attn_prefill_paged(q, P[1], P[2], P[3], P[4], qo, kvp, idx, last, B, Hq, Hkv, D, page_size,
+                                max_q_len, scale, causal, dtype, None)
+
+
+def test_prefill_paged_validation(L):
+    assert pre_paged(L, Hq=6, Hkv=4) == INVALID
+    assert pre_paged(L, page_size=24) == INVALID        # not a power of two
+    assert pre_paged(L, page_size=0) == INVALID
+    assert pre_paged(L, max_q_len=-1) == INVALID
+    assert pre_paged(L, scale=float("inf")) == INVALID
+    assert pre_paged(L, dtype=9) == INVALID
+    assert pre_paged(L, D=96) == UNSUPPORTED
+    assert pre_paged(L, dtype=F32) == UNSUPPORTED
+    assert pre_paged(L, q=None) == INVALID
+    assert pre_paged(L, idx=None) == INVALID
+    assert pre_paged(L, qo=None) == INVALID
+    assert pre_paged(L, q=ctypes.c_void_p(0x10004)) == INVALID   # misaligned
+    assert pre_paged(L, B=0) == OK
+    assert pre_paged(L, max_q_len=0) == OK
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     q = torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16)

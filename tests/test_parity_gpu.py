@@ -368,3 +368,95 @@ def test_decode_multi_dense_matches_paged():
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
     o_ref, l_ref = oracle_multi(inp, 0.125, kd, vd, block_table=None)
     check(o2, l2, o_ref, l_ref, "f16", "dense multi")
+
+
+# ---- ragged prefill over a paged cache ------------------------------------------
+
+def gpu_prefill_paged(inp, causal, scale, last=True):
+    q = inp.q.cuda()
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full(q.shape[:2], float("nan"), dtype=torch.float32, device="cuda")
+    o, l = gqa.attn_prefill_paged(q, inp.k_cache.cuda(), inp.v_cache.cuda(), inp.qo_indptr.cuda(),
+                                  inp.kv_indptr.cuda(), inp.kv_indices.cuda(), inp.max_q_len,
+                                  kv_last_page_len=inp.kv_last_page_len.cuda() if last else None,
+                                  causal=causal, scale=scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return o.double().cpu().numpy(), l.double().cpu().numpy()
+
+
+def oracle_prefill_paged(inp, causal, scale, rows=None, last=True):
+    return oracle.attn_prefill_paged(inp.q, inp.k_cache, inp.v_cache, inp.qo_indptr, inp.kv_indptr,
+                                     inp.kv_indices, scale, causal,
+                                     inp.kv_last_page_len if last else None, rows=rows)
+
+
+PAGED_PREFILL = [
+    # Hq, Hkv, D, dtype, page_size, causal, (q_lens, kv_lens) or (B, q range, prefix range)
+    (8, 2, 128, "bf16", 1, True, ([3, 0, 70, 129, 1], [9, 4, 0, 200, 300])),
+    (4, 4, 64, "f16", 16, True, (5, (1, 300), (0, 300))),        # G = 1
+    (32, 4, 128, "bf16", 64, True, (3, (1, 400), (0, 500))),      # G = 8
+    (6, 3, 64, "bf16", 256, False, (4, (1, 200), (0, 300))),      # G = 2, non-causal
+    (16, 2, 128, "f16", 4, True, ([200, 64, 7, 130], [150, 64, 3, 400])),  # some q_len > kv_len
+]
+
+
+@pytest.mark.parametrize("case", PAGED_PREFILL, ids=lambda c: "-".join(map(str, c[:6])))
+def test_prefill_paged_cases(case):
+    Hq, Hkv, D, dt, ps, causal, lens = case
+    print(f"paged prefill case {case[:6]}", flush=True)
+    if isinstance(lens[0], list):
+        inp = W.make_paged_prefill(len(lens[0]), Hq, Hkv, D, dt, seed=Hq + D + ps, page_size=ps,
+                                   q_lens=lens[0], kv_lens=lens[1])
+    else:
+        B, (qlo, qhi), (plo, phi) = lens
+        inp = W.make_paged_prefill(B, Hq, Hkv, D, dt, seed=Hq + D + ps, q_lo=qlo, q_hi=qhi,
+                                   prefix_lo=plo, prefix_hi=phi, page_size=ps)
+    scale = W.fp32_scale(D)
+    o, l = gpu_prefill_paged(inp, causal, scale)
+    o_ref, l_ref = oracle_prefill_paged(inp, causal, scale)
+    check(o, l, o_ref, l_ref, dt, str(case[:6]))
+
+
+def test_prefill_paged_full_pages_without_last_len():
+    # kv_last_page_len omitted: every page is full
+    inp = W.make_paged_prefill(3, 8, 2, 64, "bf16", seed=50, page_size=32, q_lens=[40, 64, 3],
+                               kv_lens=[64, 96, 32])
+    o, l = gpu_prefill_paged(inp, True, 0.125, last=False)
+    o_ref, l_ref = oracle_prefill_paged(inp, True, 0.125, last=False)
+    check(o, l, o_ref, l_ref, "bf16", "full pages")
+
+
+def test_prefill_paged_equals_dense_forward(monkeypatch):
+    # one request over an identity page table is the dense forward of the same K/V
+    inp = W.make_paged_prefill(1, 8, 2, 128, "bf16", seed=51, page_size=64, q_lens=[300], kv_lens=[700],
+                               permute=False)
+    o1, l1 = gpu_prefill_paged(inp, True, 0.088)
+    kd = inp.k_cache.reshape(-1, 2, 128)[:700].permute(1, 0, 2).unsqueeze(0).contiguous()
+    vd = inp.v_cache.reshape(-1, 2, 128)[:700].permute(1, 0, 2).unsqueeze(0).contiguous()
+    qd = inp.q.permute(1, 0, 2).unsqueeze(0).contiguous()
+    monkeypatch.setenv("GQA_ATTN_PREFILL_KERNEL", "fourwave")  # the kernel the paged path uses
+    o2, l2 = gpu_fwd(qd, kd, vd, True, 0.088)
+    o2 = o2.double().cpu().numpy()[0].transpose(1, 0, 2)
+    l2 = l2.double().cpu().numpy()[0].T
+    # the same kernel arithmetic on the same keys: bitwise equal
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_prefill_paged_workload_sampled():
+    spec = W.RAGGED_PAGED_PREFILL
+    print("workload ragged_paged_prefill", flush=True)
+    inp = W.make_paged_prefill_spec(spec)
+    scale = W.fp32_scale(spec.D)
+    o, l = gpu_prefill_paged(inp, spec.causal, scale)
+    total = o.shape[0] * spec.Hq
+    g = np.random.default_rng(7)
+    rows = []
+    for b in range(spec.B):  # first and last token of every request, all heads
+        t0, t1 = int(inp.qo_indptr[b]), int(inp.qo_indptr[b + 1])
+        for t in {t0, t1 - 1}:
+            rows.extend(range(t * spec.Hq, (t + 1) * spec.Hq))
+    rows = np.unique(np.concatenate([np.asarray(rows), g.choice(total, 1024, replace=False)]))
+    o_ref, l_ref = oracle_prefill_paged(inp, spec.causal, scale, rows=rows)
+    e_o, e_l = check(o.reshape(-1, spec.D)[rows], l.reshape(-1)[rows], o_ref, l_ref, "bf16",
+                     "ragged_paged_prefill")
+    print(f"ragged_paged_prefill: {len(rows)} rows, max|dO|={e_o:.3e} max|dLSE|={e_l:.3e}")
