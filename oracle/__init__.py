@@ -25,6 +25,7 @@ LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _LIB_OVERRIDE = os.environ.get("GQA_ORACLE_LIB")
 
 _DT = {torch.float64: 0, torch.float32: 1, torch.float16: 2, torch.bfloat16: 3}
+FP8_E4M3 = 4  # storage code of an 8-bit E4M3 cache given as uint8 bytes
 
 _lib = None
 
@@ -73,6 +74,9 @@ def _load():
     lib.oracle_attn_prefill_paged.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32,
                                               i32, f64, i32, vp, i64, vp, vp]
     lib.oracle_attn_prefill_paged.restype = i32
+    lib.oracle_attn_decode_fp8.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                           i32, f64, vp, i64, vp, vp]
+    lib.oracle_attn_decode_fp8.restype = i32
     _lib = lib
     return lib
 
@@ -116,11 +120,13 @@ def _rows(rows):
     return r
 
 
-def widen(t: torch.Tensor) -> np.ndarray:
-    """The oracle's own storage-format -> float64 conversion (for pinning it)."""
+def widen(t: torch.Tensor, fp8: bool = False) -> np.ndarray:
+    """The oracle's own storage-format -> float64 conversion (for pinning it);
+    fp8=True reads a uint8 tensor as E4M3 bytes."""
     t = _cpu(t)
     out = np.empty(t.numel(), dtype=np.float64)
-    _load().oracle_widen(_ptr(t), _DT[t.dtype], t.numel(), _np_ptr(out))
+    code = FP8_E4M3 if fp8 else _DT[t.dtype]
+    _load().oracle_widen(_ptr(t), code, t.numel(), _np_ptr(out))
     return out.reshape(tuple(t.shape))
 
 
@@ -292,4 +298,47 @@ def attn_prefill_paged(q, k_cache, v_cache, qo_indptr, kv_indptr, kv_indices, sc
         raise ValueError("oracle_attn_prefill_paged: bad arguments")
     if r is None:
         return o.reshape(total_q, Hq, D), lse.reshape(total_q, Hq)
+    return o, lse
+
+
+def attn_decode_fp8(q, k8, v8, k_ss, v_ss, seq_lens, scale: float, block_table=None, max_kv_len=None,
+                    rows=None):
+    """Decode over an 8-bit E4M3 KV cache with a binary16 (scale, shift) pair per
+    token row and K/V head: the key / value used is byte * scale + shift.
+
+    q [B, Hq, D] (bf16/fp16/fp32); k8, v8 uint8 [num_pages, page_size, Hkv, D]
+    (with block_table) or [B, Hkv, max_kv_len, D]; k_ss, v_ss int32/uint32
+    [num_pages, page_size, Hkv] or [B, Hkv, max_kv_len] (scale bits 0-15, shift
+    bits 16-31).  Returns (o [B, Hq, D], lse [B, Hq]) or, with rows, (o [n, D],
+    lse [n]).
+    """
+    q = _cpu(q)
+    if q.dtype not in _DT:
+        raise TypeError(f"unsupported q dtype {q.dtype}")
+    k8, v8 = _cpu(k8), _cpu(v8)
+    if k8.dtype != torch.uint8 or v8.dtype != torch.uint8:
+        raise TypeError("the fp8 cache is given as uint8 bytes")
+    kss, vss = _cpu(k_ss).view(torch.int32), _cpu(v_ss).view(torch.int32)
+    B, Hq, D = q.shape
+    sl = _cpu(seq_lens, torch.int32)
+    if block_table is not None:
+        bt = _cpu(block_table, torch.int32)
+        max_pages, page_size, Hkv = bt.shape[1], k8.shape[1], k8.shape[2]
+        if max_kv_len is None:
+            max_kv_len = max_pages * page_size
+    else:
+        bt, max_pages, page_size, Hkv = None, 0, 0, k8.shape[1]
+        if max_kv_len is None:
+            max_kv_len = k8.shape[2]
+    r = _rows(rows)
+    n = B * Hq if r is None else r.shape[0]
+    o = np.empty((n, D), dtype=np.float64)
+    lse = np.empty((n,), dtype=np.float64)
+    rc = _load().oracle_attn_decode_fp8(_ptr(q), _DT[q.dtype], _ptr(k8), _ptr(v8), _ptr(kss), _ptr(vss),
+                                        _ptr(sl), _ptr(bt), max_pages, page_size, B, Hq, Hkv, D,
+                                        int(max_kv_len), float(scale), _np_ptr(r), n, _np_ptr(o), _np_ptr(lse))
+    if rc:
+        raise ValueError("oracle_attn_decode_fp8: bad arguments")
+    if r is None:
+        return o.reshape(B, Hq, D), lse.reshape(B, Hq)
     return o, lse

@@ -45,7 +45,7 @@
 #include <omp.h>
 #endif
 
-enum { ORACLE_F64 = 0, ORACLE_F32 = 1, ORACLE_F16 = 2, ORACLE_BF16 = 3 };
+enum { ORACLE_F64 = 0, ORACLE_F32 = 1, ORACLE_F16 = 2, ORACLE_BF16 = 3, ORACLE_FP8E4M3 = 4 };
 
 /* ---- storage formats -> double ------------------------------------------ */
 
@@ -72,11 +72,29 @@ static double bf16_bits_to_double(uint16_t b) {
     return (double)f;
 }
 
+/* OCP 8-bit float E4M3 ("fn" variant): sign, 4-bit exponent (bias 7), 3-bit
+ * fraction; exponent 0 is subnormal (m * 2^-9); S.1111.111 is NaN; no
+ * infinities.  Largest finite value 448. */
+static double e4m3_bits_to_double(uint8_t b) {
+    int sign = b >> 7;
+    int e = (b >> 3) & 0xf;
+    int m = b & 0x7;
+    double v;
+    if (e == 15 && m == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp((double)(m | 0x8), e - 10);  /* 1.m * 2^(e-7) */
+    return sign ? -v : v;
+}
+
 static double elem(const void* base, int64_t idx, int dt) {
     switch (dt) {
     case ORACLE_F64: return ((const double*)base)[idx];
     case ORACLE_F32: return (double)((const float*)base)[idx];
     case ORACLE_F16: return half_bits_to_double(((const uint16_t*)base)[idx]);
+    case ORACLE_FP8E4M3: return e4m3_bits_to_double(((const uint8_t*)base)[idx]);
     default:         return bf16_bits_to_double(((const uint16_t*)base)[idx]);
     }
 }
@@ -111,7 +129,25 @@ typedef struct {
     int page_size;
     int Hkv;
     int g;
+    /* fp8 cache: per (token row, K/V head) a uint32 holding two binary16,
+     * the scale in bits 0-15 and the shift in bits 16-31 ([P4]
+     * `cast_uint32_to_half2`); NULL for an unquantized cache */
+    const uint32_t* k_ss;
+    const uint32_t* v_ss;
 } kv_view;
+
+static int64_t kv_index(const kv_view* kv, int64_t t, int d);
+
+/* [P4] `dequantize` (fp8 branch): value = stored * scale + shift, with the
+ * scale and shift of the element's token row and head; the index of that pair
+ * is the element index divided by D (one pair per D-element row). */
+static double kv_value(const kv_view* kv, const void* base, const uint32_t* ss, int64_t t, int d) {
+    int64_t idx = kv_index(kv, t, d);
+    double x = elem(base, idx, kv->dt);
+    if (!ss) return x;
+    uint32_t w = ss[idx / kv->D];
+    return x * half_bits_to_double((uint16_t)(w & 0xffff)) + half_bits_to_double((uint16_t)(w >> 16));
+}
 
 static int64_t kv_index(const kv_view* kv, int64_t t, int d) {
     if (kv->bt_row) {
@@ -151,7 +187,7 @@ static void attend_one(const void* q, int64_t q_off, int q_dt, const kv_view* kv
     for (int64_t t = lo; t < end; ++t) {
         double acc = 0.0;
         for (int d = 0; d < D; ++d)
-            acc += elem(q, q_off + d, q_dt) * elem(kv->k, kv_index(kv, t, d), kv->dt);
+            acc += elem(q, q_off + d, q_dt) * kv_value(kv, kv->k, kv->k_ss, t, d);
         s[t - lo] = scale * acc;
     }
     double m = -INFINITY;
@@ -164,7 +200,7 @@ static void attend_one(const void* q, int64_t q_off, int q_dt, const kv_view* kv
     for (int64_t t = lo; t < end; ++t) {
         double p = exp(s[t - lo] - L);
         if (p_out) p_out[t - lo] = p;
-        for (int d = 0; d < D; ++d) o[d] += p * elem(kv->v, kv_index(kv, t, d), kv->dt);
+        for (int d = 0; d < D; ++d) o[d] += p * kv_value(kv, kv->v, kv->v_ss, t, d);
     }
 }
 
@@ -206,7 +242,7 @@ int oracle_attn_fwd(const void* q, const void* k, const void* v, int dt,
             int b = (int)(bh / Hq);
             int g = h / group;
             kv_view kv = {k, v, dt, D, ((int64_t)b * Hkv + g) * kv_len * (int64_t)D,
-                          NULL, 0, Hkv, g};
+                          NULL, 0, Hkv, g, NULL, NULL};
             int64_t vis_end = causal ? i + 1 + delta : (int64_t)kv_len;
             attend_one(q, r * (int64_t)D, dt, &kv, 0, kv_len, vis_end, scale, s,
                        o_out + n * (int64_t)D, lse_out + n, NULL);
@@ -231,7 +267,7 @@ int oracle_softmax_matrix(const void* q, const void* k, int dt,
     double* s = (double*)malloc(sizeof(double) * (size_t)(kv_len > 0 ? kv_len : 1));
     double* o = (double*)malloc(sizeof(double) * (size_t)D);
     /* V is not needed for P; point it at K so the accumulation is harmless. */
-    kv_view kv = {k, k, dt, D, ((int64_t)b * Hkv + g) * kv_len * (int64_t)D, NULL, 0, Hkv, g};
+    kv_view kv = {k, k, dt, D, ((int64_t)b * Hkv + g) * kv_len * (int64_t)D, NULL, 0, Hkv, g, NULL, NULL};
     for (int64_t i = 0; i < q_len; ++i) {
         double lse;
         int64_t vis_end = causal ? i + 1 + delta : (int64_t)kv_len;
@@ -277,7 +313,7 @@ int oracle_attn_decode(const void* q, const void* k, const void* v, int dt,
             if (len < 0 || len > max_kv_len) { bad = 1; continue; }
             kv_view kv = {k, v, dt, D, ((int64_t)b * Hkv + g) * max_kv_len * (int64_t)D,
                           block_table ? block_table + (int64_t)b * max_pages : NULL,
-                          page_size, Hkv, g};
+                          page_size, Hkv, g, NULL, NULL};
             attend_one(q, r * (int64_t)D, dt, &kv, 0, len, len, scale, s,
                        o_out + n * (int64_t)D, lse_out + n, NULL);
         }
@@ -323,7 +359,7 @@ int oracle_attn_decode_multi(const void* q, const void* k, const void* v, int dt
             if (len < 0 || len > max_kv_len) { bad = 1; continue; }
             kv_view kv = {k, v, dt, D, ((int64_t)b * Hkv + g) * max_kv_len * (int64_t)D,
                           block_table ? block_table + (int64_t)b * max_pages : NULL,
-                          page_size, Hkv, g};
+                          page_size, Hkv, g, NULL, NULL};
             /* position of query i: len - q_len + i; keys t <= that position */
             int64_t vis_end = len - q_len + i + 1;
             attend_one(q, r * (int64_t)D, dt, &kv, 0, len, vis_end, scale, s,
@@ -384,9 +420,55 @@ int oracle_attn_prefill_paged(const void* q, const void* k, const void* v, int d
             if (n_pages > 0)
                 kv_len = (n_pages - 1) * page_size + (kv_last_page_len ? kv_last_page_len[b] : page_size);
             int g = h / group;
-            kv_view kv = {k, v, dt, D, 0, kv_indices + kv_indptr[b], page_size, Hkv, g};
+            kv_view kv = {k, v, dt, D, 0, kv_indices + kv_indptr[b], page_size, Hkv, g, NULL, NULL};
             int64_t vis_end = causal ? i + 1 + (kv_len - q_len) : kv_len;
             attend_one(q, r * (int64_t)D, dt, &kv, 0, kv_len, vis_end, scale, s,
+                       o_out + n * (int64_t)D, lse_out + n, NULL);
+        }
+        free(s);
+    }
+    return bad;
+}
+
+/*
+ * Decode over an fp8 KV cache.  [P4] `_fwd_kernel_splitK` with FP8_QUANTIZED:
+ * K and V hold one 8-bit float per element (E4M3) and every (token, K/V head)
+ * row has a binary16 scale and shift, so the key or value used is
+ * stored * scale + shift (`dequantize`); attention is then the plain decode
+ * of oracle_attn_decode over those values, in double.  q (and the output) are
+ * in q_dt.  k_ss / v_ss are laid out like the cache without its last
+ * dimension: [num_pages, page_size, Hkv] (paged) or [B, Hkv, max_kv_len]
+ * (dense).
+ */
+int oracle_attn_decode_fp8(const void* q, int q_dt, const void* k, const void* v,
+                           const uint32_t* k_ss, const uint32_t* v_ss,
+                           const int* seq_lens, const int* block_table, int max_pages,
+                           int page_size, int B, int Hq, int Hkv, int D, int max_kv_len,
+                           double scale, const int64_t* rows, int64_t n_rows,
+                           double* o_out, double* lse_out) {
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv || max_kv_len < 0) return 1;
+    if (!k_ss || !v_ss) return 1;
+    if (block_table && (page_size <= 0 || max_pages <= 0)) return 1;
+    const int64_t total = (int64_t)B * Hq;
+    if (!rows) n_rows = total;
+    const int group = Hq / Hkv;
+    int bad = 0;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)(max_kv_len > 0 ? max_kv_len : 1));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t n = 0; n < n_rows; ++n) {
+            int64_t r = rows ? rows[n] : n;
+            if (r < 0 || r >= total) { bad = 1; continue; }
+            int h = (int)(r % Hq);
+            int b = (int)(r / Hq);
+            int g = h / group;
+            int64_t len = seq_lens[b];
+            if (len < 0 || len > max_kv_len) { bad = 1; continue; }
+            kv_view kv = {k, v, ORACLE_FP8E4M3, D, ((int64_t)b * Hkv + g) * max_kv_len * (int64_t)D,
+                          block_table ? block_table + (int64_t)b * max_pages : NULL,
+                          page_size, Hkv, g, k_ss, v_ss};
+            attend_one(q, r * (int64_t)D, q_dt, &kv, 0, len, len, scale, s,
                        o_out + n * (int64_t)D, lse_out + n, NULL);
         }
         free(s);
@@ -432,7 +514,7 @@ int oracle_decode_split_merge(const void* q, const void* k, const void* v, int d
             if (len < 0 || len > max_kv_len) { bad = 1; continue; }
             kv_view kv = {k, v, dt, D, ((int64_t)b * Hkv + g) * max_kv_len * (int64_t)D,
                           block_table ? block_table + (int64_t)b * max_pages : NULL,
-                          page_size, Hkv, g};
+                          page_size, Hkv, g, NULL, NULL};
             const int* bb = bounds + (int64_t)b * (n_splits + 1);
             for (int sp = 0; sp < n_splits; ++sp) {
                 int64_t lo = bb[sp], hi = bb[sp + 1];

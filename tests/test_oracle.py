@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import oracle
-from workloads import make_prefill, make_decode, make_paged_prefill, fp32_scale
+from workloads import make_prefill, make_decode, make_paged_prefill, make_decode_fp8, fp32_scale
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 TOL = 1e-12
@@ -438,3 +438,49 @@ def test_paged_prefill_equals_dense_forward():
                                        inp.kv_indices, 0.2, True, inp.kv_last_page_len)
     o2, l2 = oracle.attn_fwd(qd, kd, vd, 0.2, True)
     assert np.array_equal(o1, o2[0].transpose(1, 0, 2)) and np.array_equal(l1, l2[0].T)
+
+
+# ---- decode over an 8-bit E4M3 cache ---------------------------------------------
+
+def test_widen_every_e4m3_pattern():
+    b = torch.arange(256, dtype=torch.uint8)
+    got = oracle.widen(b, fp8=True)
+    ref = b.view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[~np.isnan(ref)], ref[~np.isnan(ref)])
+
+
+def _dequant(x8, ss):
+    """x8 * scale + shift in fp64, with torch's own E4M3 and fp16 decoding."""
+    ss = ss.to(torch.int32)
+    sc = (ss & 0xFFFF).to(torch.int16).view(torch.float16).double()
+    sh = ((ss >> 16) & 0xFFFF).to(torch.int16).view(torch.float16).double()
+    return x8.view(torch.float8_e4m3fn).double() * sc[..., None] + sh[..., None]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_decode_fp8_matches_torch_on_dequantized_cache(dtype):
+    inp = make_decode_fp8(3, 8, 2, 16, dtype, seed=60, len_lo=1, len_hi=40, page_size=8)
+    o, l = oracle.attn_decode_fp8(inp.q, inp.k8, inp.v8, inp.k_ss, inp.v_ss, inp.seq_lens, 0.25,
+                                  block_table=inp.block_table)
+    kd_all, vd_all = _dequant(inp.k8, inp.k_ss), _dequant(inp.v8, inp.v_ss)
+    for b in range(3):
+        n = int(inp.seq_lens[b])
+        pages = inp.block_table[b, :(n + 7) // 8].long()
+        kd = kd_all[pages].reshape(-1, 2, 16)[:n].permute(1, 0, 2).unsqueeze(0).contiguous()
+        vd = vd_all[pages].reshape(-1, 2, 16)[:n].permute(1, 0, 2).unsqueeze(0).contiguous()
+        o_ref, l_ref = torch_reference(inp.q[b].view(1, 8, 1, 16), kd, vd, 0.25, True)
+        np.testing.assert_allclose(o[b], o_ref[0, :, 0], atol=TOL, rtol=0)
+        np.testing.assert_allclose(l[b], l_ref[0, :, 0], atol=TOL, rtol=0)
+
+
+def test_decode_fp8_unit_scale_is_plain_decode():
+    # scale 1, shift 0: the E4M3 values themselves, which bf16 holds exactly
+    inp = make_decode_fp8(2, 4, 2, 32, "bf16", seed=61, len_lo=5, len_hi=50, page_size=16)
+    one = torch.full_like(inp.k_ss, 0x3C00)  # fp16 1.0 in bits 0-15, +0.0 in bits 16-31
+    o1, l1 = oracle.attn_decode_fp8(inp.q, inp.k8, inp.v8, one, one, inp.seq_lens, 0.2,
+                                    block_table=inp.block_table)
+    kb = inp.k8.view(torch.float8_e4m3fn).to(torch.bfloat16)
+    vb = inp.v8.view(torch.float8_e4m3fn).to(torch.bfloat16)
+    o2, l2 = oracle.attn_decode(inp.q, kb, vb, inp.seq_lens, 0.2, block_table=inp.block_table)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)

@@ -41,6 +41,10 @@ MUTANTS = {
                                    "int64_t vis_end = len - i;"),
     "paged_prefill_last_page_ignored": ("kv_len = (n_pages - 1) * page_size + (kv_last_page_len ? kv_last_page_len[b] : page_size);",
                                         "kv_len = n_pages * page_size;"),
+    "e4m3_exponent_bias": ("v = ldexp((double)(m | 0x8), e - 10);", "v = ldexp((double)(m | 0x8), e - 9);"),
+    "e4m3_subnormal_scale": ("v = ldexp((double)m, -9);", "v = ldexp((double)m, -10);"),
+    "fp8_scale_shift_swapped": ("return x * half_bits_to_double((uint16_t)(w & 0xffff)) + half_bits_to_double((uint16_t)(w >> 16));",
+                                "return x * half_bits_to_double((uint16_t)(w >> 16)) + half_bits_to_double((uint16_t)(w & 0xffff));"),
     "paged_prefill_top_left": ("int64_t vis_end = causal ? i + 1 + (kv_len - q_len) : kv_len;",
                                "int64_t vis_end = causal ? i + 1 : kv_len;"),
 }

@@ -16,6 +16,8 @@ Workloads (shapes of the attention problems the pages state):
   paged_decode          B=16 Hq=32 Hkv=8 D=128, bf16, kv_len ~ U[1024, 32768],
                         256-token pages placed by a seeded permutation, 16 splits
   multi_query_decode    the same with 4 queries per sequence at its last positions
+  fp8_paged_decode      paged_decode over an 8-bit E4M3 K/V cache with a binary16
+                        (scale, shift) pair per token row and K/V head
   ragged_paged_prefill  8 requests, Hq=32 Hkv=4 D=128, bf16, causal; request b has
                         q_len ~ U[256, 2048] new tokens after a cached prefix of
                         U[0, 2048] tokens; one token per page, pages placed by a
@@ -75,6 +77,7 @@ CAUSAL_GQA_PREFILL = PrefillSpec("causal_gqa_prefill", 2, 32, 8, 2048, 2048, 128
 CAUSAL_GQA_OFFSET = PrefillSpec("causal_gqa_offset", 1, 32, 4, 1024, 4096, 128, "bf16", True, 20263)
 MHA_NONCAUSAL_FP16 = PrefillSpec("mha_noncausal_fp16", 4, 16, 16, 4096, 4096, 64, "f16", False, 20264, 0.5)
 PAGED_DECODE = DecodeSpec("paged_decode", 16, 32, 8, 128, "bf16", 1024, 32768, 256, 128, 16, 20265)
+FP8_PAGED_DECODE = DecodeSpec("fp8_paged_decode", 16, 32, 8, 128, "bf16", 1024, 32768, 256, 128, 16, 20268)
 MULTI_QUERY_DECODE = DecodeSpec("multi_query_decode", 16, 32, 8, 128, "bf16", 1024, 32768, 256, 128, 16,
                                 20266, q_len=4)
 
@@ -227,3 +230,47 @@ def make_paged_prefill(B, Hq, Hkv, D, dtype="bf16", seed=0, q_lo=1, q_hi=64, pre
 def make_paged_prefill_spec(spec: PagedPrefillSpec):
     return make_paged_prefill(spec.B, spec.Hq, spec.Hkv, spec.D, spec.dtype, spec.seed, spec.q_lo, spec.q_hi,
                               spec.prefix_lo, spec.prefix_hi, spec.page_size)
+
+
+@dataclass
+class DecodeFp8Inputs:
+    q: torch.Tensor            # [B, Hq, D] (bf16 / fp16)
+    k8: torch.Tensor           # [num_pages, page_size, Hkv, D] uint8 (E4M3 bytes)
+    v8: torch.Tensor
+    k_ss: torch.Tensor         # [num_pages, page_size, Hkv] int32: fp16 scale bits 0-15, shift bits 16-31
+    v_ss: torch.Tensor
+    seq_lens: torch.Tensor     # [B] int32
+    block_table: torch.Tensor  # [B, max_pages] int32, -1 padding
+    page_size: int
+    max_kv_len: int
+
+
+def quantize_e4m3_rows(x: torch.Tensor):
+    """Per row (last dimension): shift = row mean and scale = max |x - shift| / 448,
+    both rounded to fp16; bytes = E4M3(x - shift) / scale), rounded by torch's
+    cast.  Returns (uint8 bytes, int32 words with the scale in bits 0-15 and the
+    shift in bits 16-31)."""
+    shift = x.mean(dim=-1, keepdim=True).to(torch.float16)
+    dev = (x - shift.float()).abs().amax(dim=-1, keepdim=True)
+    scale = torch.where(dev > 0, dev / 448.0, torch.ones_like(dev)).to(torch.float16)
+    q8 = ((x - shift.float()) / scale.float()).to(torch.float8_e4m3fn).view(torch.uint8)
+    sb = scale.view(torch.int16).to(torch.int32) & 0xFFFF
+    hb = shift.view(torch.int16).to(torch.int32) & 0xFFFF
+    return q8, (sb | (hb << 16)).squeeze(-1)
+
+
+def make_decode_fp8(B, Hq, Hkv, D, dtype="bf16", seed=0, len_lo=1, len_hi=64, page_size=256,
+                    max_pages: Optional[int] = None, seq_lens=None, permute=True):
+    """Paged decode inputs with an E4M3 K/V cache: drawn like make_decode (q,
+    seq_lens, page permutation, K, V in fp32 N(0, 1)), then every (token, head)
+    row of K and V quantized by quantize_e4m3_rows."""
+    base = make_decode(B, Hq, Hkv, D, "f32", seed, len_lo, len_hi, page_size, max_pages, seq_lens, permute)
+    k8, kss = quantize_e4m3_rows(base.k_cache)
+    v8, vss = quantize_e4m3_rows(base.v_cache)
+    return DecodeFp8Inputs(base.q.to(_DTYPES[dtype]), k8, v8, kss, vss, base.seq_lens, base.block_table,
+                           page_size, base.max_kv_len)
+
+
+def make_decode_fp8_spec(spec: DecodeSpec):
+    return make_decode_fp8(spec.B, spec.Hq, spec.Hkv, spec.D, spec.dtype, spec.seed, spec.len_lo, spec.len_hi,
+                           spec.page_size, spec.max_pages)
