@@ -5,9 +5,9 @@ Prints ONE JSON line.  The headline workload is causal GQA prefill in bf16
 batch, inputs already resident in HBM.  `value` is TFLOP/s counted on the
 visible (query, key) pairs only (4*D flop per pair; masked work is not
 credited).  The other workloads (fp32 correctness shape, bottom-right offset
-prefill, non-causal fp16 MHA, split-K paged decode with one and with four
-queries per sequence, ragged prefill over a paged cache) are timed the same way
-and reported under "workloads".
+prefill, non-causal fp16 MHA, split-K paged decode over a 16-bit and over an
+E4M3 cache, decode with four queries per sequence, ragged prefill over a paged
+cache) are timed the same way and reported under "workloads".
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--only NAME]
 """
@@ -75,11 +75,12 @@ def prefill_flops(spec) -> int:
     return 4 * spec.D * spec.B * spec.Hq * visible_pairs(spec.q_len, spec.kv_len, spec.causal)
 
 
-def decode_bytes(spec, inp) -> int:
+def decode_bytes(spec, inp, fp8=False) -> int:
     elt = 2
     tokens = int(inp.seq_lens.to(torch.int64).sum())
     pages = int(sum((int(s) + spec.page_size - 1) // spec.page_size for s in inp.seq_lens))
-    kv = 2 * tokens * spec.Hkv * spec.D * elt
+    # K and V: 16-bit elements, or E4M3 bytes plus one 4-byte scale-shift word per token row and head
+    kv = 2 * tokens * spec.Hkv * (spec.D + 4 if fp8 else spec.D * elt)
     qo = 2 * spec.B * spec.Hq * spec.q_len * spec.D * elt
     lse = spec.B * spec.Hq * spec.q_len * 4
     meta = 4 * pages + 4 * spec.B
@@ -147,6 +148,41 @@ def bench_prefill(spec, steps, warmup):
 
 
 COPY_BYTES = 512 << 20
+
+
+def bench_decode_fp8(spec, steps, warmup):
+    inp = W.make_decode_fp8_spec(spec)
+    dev = torch.device("cuda:0")
+    q = inp.q.to(dev)
+    k8, v8, kss, vss = (t.to(dev) for t in (inp.k8, inp.v8, inp.k_ss, inp.v_ss))
+    sl, bt = inp.seq_lens.to(dev), inp.block_table.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    ws = torch.empty(gqa.decode_workspace_bytes(spec.B, spec.Hq, spec.D, spec.n_splits), dtype=torch.uint8,
+                     device=dev)
+    scale = W.fp32_scale(spec.D)
+
+    def step():
+        gqa.attn_decode_splitk_fp8(q, k8, v8, kss, vss, sl, block_table=bt, n_splits=spec.n_splits, scale=scale,
+                                   max_kv_len=inp.max_kv_len, workspace=ws, out=o, lse=lse)
+
+    wall, kern_s, per = time_launches(step, steps, warmup)
+    nbytes = decode_bytes(spec, inp, fp8=True)
+    tokens = int(inp.seq_lens.to(torch.int64).sum())
+    return {
+        "workload": spec.name, "dtype": "e4m3 K/V, " + spec.dtype + " q/o",
+        "shape": {"B": spec.B, "Hq": spec.Hq, "Hkv": spec.Hkv, "D": spec.D, "page_size": spec.page_size,
+                  "n_splits": spec.n_splits, "sum_kv_len": tokens},
+        "bytes_per_step": nbytes,
+        "workspace_bytes_rw": 2 * spec.B * spec.Hq * spec.n_splits * (spec.D + 1) * 4,
+        "ms_per_step": wall / steps * 1e3,
+        "kernel_ms_mean": kern_s * 1e3, "kernel_ms_min": float(per.min()) * 1e3,
+        "gbps": nbytes * steps / wall / 1e9,
+        "kernel_gbps": nbytes / kern_s / 1e9,
+        "tokens_per_s": tokens / kern_s,
+        "peak_gbps": PEAK_HBM_GBPS,
+        "frac_of_peak": nbytes / kern_s / 1e9 / PEAK_HBM_GBPS,
+    }
 
 
 def bench_paged_prefill(spec, steps, warmup):
@@ -262,6 +298,8 @@ def cpu_baseline(spec, target_s=12.0):
 
 
 def run_one(spec, steps, warmup):
+    if spec is W.FP8_PAGED_DECODE:
+        return bench_decode_fp8(spec, steps, warmup)
     if isinstance(spec, W.DecodeSpec):
         return bench_decode(spec, steps, warmup)
     if isinstance(spec, W.PagedPrefillSpec):
@@ -289,7 +327,8 @@ def main():
         sys.exit(2)
 
     all_specs = [W.CAUSAL_GQA_FP32, W.CAUSAL_GQA_PREFILL, W.CAUSAL_GQA_OFFSET,
-                 W.MHA_NONCAUSAL_FP16, W.PAGED_DECODE, W.MULTI_QUERY_DECODE, W.RAGGED_PAGED_PREFILL]
+                 W.MHA_NONCAUSAL_FP16, W.PAGED_DECODE, W.FP8_PAGED_DECODE, W.MULTI_QUERY_DECODE,
+                 W.RAGGED_PAGED_PREFILL]
     if args.only == "hbm_copy":
         print(json.dumps(bench_copy(args.steps, args.warmup)), flush=True)
         return

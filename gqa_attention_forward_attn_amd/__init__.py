@@ -24,6 +24,7 @@ _TORCH_DT = {torch.float32: GQA_F32, torch.float16: GQA_F16, torch.bfloat16: GQA
 
 # Every symbol include/gqa_attn.h declares.
 EXPORTS = ("attn_fwd", "attn_prefill_paged", "attn_decode_workspace_bytes", "attn_decode_splitk",
+           "attn_decode_splitk_fp8",
            "attn_decode_workspace_bytes_multi", "attn_decode_splitk_multi", "attn_status_str")
 
 _lib = None
@@ -60,6 +61,9 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_splitk_multi.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                            i32, f32, i32, vp, sz, i32, vp]
     L.attn_decode_splitk_multi.restype = i32
+    L.attn_decode_splitk_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                         i32, f32, i32, vp, sz, i32, vp]
+    L.attn_decode_splitk_fp8.restype = i32
     L.attn_status_str.argtypes = [i32]
     L.attn_status_str.restype = ctypes.c_char_p
     _lib = L
@@ -201,6 +205,44 @@ def attn_decode_splitk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_le
                                   workspace.numel() * workspace.element_size(),
                                   _TORCH_DT[q.dtype], _stream(q.device))
     _check("attn_decode_splitk", rc)
+    return out, lse
+
+
+def attn_decode_splitk_fp8(q: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, k_scale_shift: torch.Tensor,
+                           v_scale_shift: torch.Tensor, seq_lens: torch.Tensor,
+                           block_table: Optional[torch.Tensor] = None, n_splits: int = 16,
+                           scale: Optional[float] = None, max_kv_len: Optional[int] = None,
+                           workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                           lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Split-K decode over an E4M3 KV cache. q [B,Hq,D] bf16/fp16; k8/v8 uint8
+    [pages,page_size,Hkv,D] with block_table (page_size >= 16) or [B,Hkv,max_kv_len,D];
+    k/v_scale_shift int32 [pages,page_size,Hkv] or [B,Hkv,max_kv_len] (binary16
+    scale in bits 0-15, shift in bits 16-31).  Returns (o [B,Hq,D], lse [B,Hq])."""
+    B, Hq, D = q.shape
+    Hkv, page_size, max_pages, max_kv_len = _decode_layout(k8, block_table, max_kv_len)
+    if seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous():
+        raise TypeError("seq_lens must be a contiguous int32 tensor")
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("q must be bfloat16 or float16")
+    if k8.dtype != torch.uint8 or v8.dtype != torch.uint8:
+        raise TypeError("the E4M3 cache is passed as uint8 bytes")
+    for t in (k_scale_shift, v_scale_shift):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise TypeError("scale-shift words must be contiguous int32 tensors")
+    need = decode_workspace_bytes(B, Hq, D, n_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    sc = default_scale(D) if scale is None else float(scale)
+    rc = lib().attn_decode_splitk_fp8(_ptr(q), _ptr(k8), _ptr(v8), _ptr(k_scale_shift), _ptr(v_scale_shift),
+                                      _ptr(out), _ptr(lse), _ptr(seq_lens), _ptr(block_table), max_pages,
+                                      page_size, B, Hq, Hkv, D, max_kv_len, sc, int(n_splits), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _TORCH_DT[q.dtype],
+                                      _stream(q.device))
+    _check("attn_decode_splitk_fp8", rc)
     return out, lse
 
 

@@ -163,6 +163,54 @@ gqa_status_t attn_decode_splitk_multi(const void* q, const void* k, const void* 
     return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 
+gqa_status_t attn_decode_splitk_fp8(const void* q, const void* k_cache, const void* v_cache,
+                                    const uint32_t* k_scale_shift, const uint32_t* v_scale_shift,
+                                    void* o, float* lse, const int* seq_lens, const int* block_table,
+                                    int max_pages_per_seq, int page_size, int B, int Hq, int Hkv, int D,
+                                    int max_kv_len, float scale, int n_splits, void* workspace,
+                                    size_t workspace_bytes, gqa_dtype_t dtype, void* hip_stream) {
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || max_kv_len < 0) return GQA_ERR_INVALID_ARG;
+    if (Hq % Hkv != 0) return GQA_ERR_INVALID_ARG;
+    if (n_splits < 1 || n_splits > 256) return GQA_ERR_INVALID_ARG;
+    if (!valid_dtype(dtype)) return GQA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return GQA_ERR_INVALID_ARG;
+    int page_shift = 0;
+    if (block_table) {
+        if (page_size <= 0 || (page_size & (page_size - 1)) != 0 || max_pages_per_seq <= 0)
+            return GQA_ERR_INVALID_ARG;
+        if ((long long)max_pages_per_seq * page_size < (long long)max_kv_len) return GQA_ERR_INVALID_ARG;
+        while ((1 << page_shift) < page_size) ++page_shift;
+    }
+    if (!supported_head_dim(D) || dtype == GQA_F32) return GQA_ERR_UNSUPPORTED;
+    if (block_table && page_size < 16) return GQA_ERR_UNSUPPORTED;  // a 16-token slice must fit in a page
+    if (B == 0) return GQA_OK;
+    if (!q || !k_cache || !v_cache || !k_scale_shift || !v_scale_shift || !o || !lse || !seq_lens)
+        return GQA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return GQA_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(k_scale_shift) & 3u) || (reinterpret_cast<uintptr_t>(v_scale_shift) & 3u))
+        return GQA_ERR_INVALID_ARG;
+    const size_t need = attn_decode_workspace_bytes(B, Hq, D, n_splits);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return GQA_ERR_WORKSPACE;
+
+    gqa::DecodeArgs a{};
+    a.q = q; a.k = k_cache; a.v = v_cache; a.o = o; a.lse = lse;
+    a.k_ss = k_scale_shift;
+    a.v_ss = v_scale_shift;
+    a.seq_lens = seq_lens;
+    a.block_table = block_table;
+    a.part_o = static_cast<float*>(workspace);
+    a.part_lse = a.part_o + (size_t)B * Hq * n_splits * D;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.group = Hq / Hkv;
+    a.q_len = 1;
+    a.max_pages = max_pages_per_seq;
+    a.page_shift = page_shift;
+    a.max_kv_len = max_kv_len;
+    a.n_splits = n_splits;
+    a.c = scale * kLog2e;
+    hipError_t e = gqa::launch_decode_fp8(a, to_kernel_dtype(dtype), static_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
 gqa_status_t attn_decode_splitk(const void* q, const void* k, const void* v, void* o, float* lse,
                                 const int* seq_lens, const int* block_table,
                                 int max_pages_per_seq, int page_size,

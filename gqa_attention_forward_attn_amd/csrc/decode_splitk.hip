@@ -59,6 +59,13 @@ enum { kDense = 0, kPaged = 1, kPagedSmall = 2 };
 #ifndef DEC_NST
 #define DEC_NST 4
 #endif
+// waves and ring stages of the E4M3 split kernel
+#ifndef DEC8_NW
+#define DEC8_NW 4
+#endif
+#ifndef DEC8_NST
+#define DEC8_NST 2
+#endif
 
 // Chunk length of the split-K partition (a multiple of 64 tokens); both kernels
 // derive the chunk bounds from it.
@@ -394,6 +401,333 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
     }
 }
 
+// ---- split kernel over an 8-bit E4M3 K/V cache ---------------------------------
+//
+// splitk_kernels.py, `_fwd_kernel_splitK` with FP8_QUANTIZED: K and V hold one
+// E4M3 byte per element and every (token, K/V head) row carries a binary16
+// scale and shift packed in a uint32 (`cast_uint32_to_half2`); the value used
+// is byte * scale + shift (`dequantize`).  The affine map is folded out of the
+// two contractions, so the matrix cores see the E4M3 values themselves (bf16
+// and fp16 hold them exactly):
+//   s_t = scale_t * (q . x_t) + shift_t * sum_d q_d
+//   O   = (sum_t (p_t scale_t) x_t + sum_t p_t shift_t) / l
+// Per 16-token slice, the K and V bytes (16 x D each) and the slice's 32 scale /
+// shift words come by direct loads into the wave's LDS ring; the K operand is
+// converted to 16-bit floats in registers (v_cvt_scalef32_pk_*_fp8 with scale
+// 1), and the V slice is converted once into a 16-bit slice buffer that the
+// transposed reads of the P.V product use as in decode_split_kernel.
+
+// 4 bytes per lane from global memory into LDS (lane i -> lds + 4 i).
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds) {
+    __asm__ __volatile__("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+                         :
+                         : "v"(gptr), "s"(lds)
+                         : "m0", "memory");
+}
+
+// Four E4M3 bytes (one dword, element order = byte order) -> four 16-bit floats.
+__device__ __forceinline__ u32x2 e4m3x4_to16(bf16_tag, uint32_t w) {
+    return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))};
+}
+__device__ __forceinline__ u32x2 e4m3x4_to16(f16_tag, uint32_t w) {
+    return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true))};
+}
+// Sum of the two 16-bit floats of a dword.
+__device__ __forceinline__ float pair_sum(bf16_tag, uint32_t w) {
+    return __builtin_bit_cast(float, w << 16) + __builtin_bit_cast(float, w & 0xffff0000u);
+}
+__device__ __forceinline__ float pair_sum(f16_tag, uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffff)) +
+           (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+// binary16 in bits 0-15 / 16-31 of a scale-shift word
+__device__ __forceinline__ float half_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffff)); }
+__device__ __forceinline__ float half_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
+// E4M3 K/V slices: rows of D bytes; 16-byte chunk c of row r at position
+// c ^ swz8<D>(r).  D = 128 (two rows per 64-bank row): a bijection on
+// (r >> 1) % 8 as swz<64>; D = 64 (four rows per bank row): (r >> 2) % 4.  The
+// 8-byte K operand reads (16 lanes = 16 rows at one column) then hit 16
+// distinct bank groups.
+template <int D>
+__device__ __forceinline__ int swz8(int r) {
+    if (D == 128) return swz<64>(r);
+    return (r >> 2) & 3;
+}
+
+template <class TAG, int D, int NW, int NST, int PG>
+__global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel_fp8(DecodeArgs a) {
+    constexpr int QROWB = 2 * D;            // bytes per q row (16-bit floats)
+    constexpr int KROWB = D;                // bytes per E4M3 K / V row
+    constexpr int CPR = KROWB / 16;         // 16-byte chunks per K / V row
+    constexpr int RPI = 64 / CPR;           // rows per direct-load instruction
+    constexpr int NI = kSlice / RPI;        // direct loads per slice, each of K and V
+    constexpr int SLB = kSlice * KROWB;     // bytes of a K (or V) slice
+    constexpr int SSB = 256;                // scale-shift words: K at 0, V at 64 (rest repeats)
+    constexpr int STB = 2 * SLB + SSB;      // stage
+    constexpr int QB = 16 * QROWB;          // q rows of the head block
+    constexpr int VCB = kSlice * QROWB;     // the current V slice in 16-bit floats
+    constexpr int WAVEB = QB + NST * STB + VCB;
+    constexpr int KS = D / 32;
+    constexpr int NB = D / 16;
+    constexpr int PER_SLICE = 2 * NI + 1;
+    constexpr int SCH = D / 64;             // E4M3 V chunks each lane converts per slice
+    constexpr int QCPR = QROWB / 16;        // q: chunks per row, rows per load
+    constexpr int QRPI = 64 / QCPR;
+    static_assert(PG != kPagedSmall, "E4M3 pages hold at least one 16-token slice");
+    static_assert((NST - 1) * PER_SLICE < 64, "vmcnt range");
+    static_assert((NST & (NST - 1)) == 0, "NST must be a power of two");
+    static_assert(NW * 16 * (D + 3) * 4 <= NW * WAVEB, "merge buffers must fit in the ring");
+
+    __shared__ __attribute__((aligned(1024))) char smem_raw[NW * WAVEB];
+    lds_char* smem = (lds_char*)smem_raw;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    // ---- work item: (b, split, head block, kv head), kv head fastest ----------
+    const int ncol = a.group;               // one query per sequence: a column per head
+    const int n_hb = (ncol + 15) >> 4;
+    int id = blockIdx.x;
+    const int g = id % a.Hkv;
+    id /= a.Hkv;
+    const int hb = id % n_hb;
+    id /= n_hb;
+    const int s = id % a.n_splits;
+    const int b = id / a.n_splits;
+    const int nh = min(16, ncol - hb * 16);
+    const size_t qrow0 = (size_t)b * a.Hq + (size_t)g * a.group + hb * 16;
+
+    const int len = a.seq_lens[b];
+    if (len <= 0) return;
+    const int chunk = chunk_tokens(len, a.n_splits);
+    const int lo = s * chunk;
+    if (lo >= len) return;  // empty chunk: the combine kernel skips it
+    const int hi = min(len, lo + chunk);
+
+    const int stride = kSlice * NW;
+    const int span = hi - lo;
+    const int n_sl = span > kSlice * wave ? (span - kSlice * wave + stride - 1) / stride : 0;
+    const int T0 = lo + kSlice * wave;
+
+    const lds_char* wlds = smem + wave * WAVEB;
+    const uint32_t wlds_u = (uint32_t)(uintptr_t)wlds;
+    lds_char* vcs = smem + wave * WAVEB + QB + NST * STB;  // 16-bit V slice
+
+    // direct loads: lane -> (row in instruction, physical chunk)
+    const int drow = lane / CPR;
+    const int dchk = lane % CPR;
+    int urow[NI], lcol[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        urow[i] = RPI * i + drow;
+        lcol[i] = (dchk ^ swz8<D>(urow[i])) * 16;  // byte offset of the logical chunk
+    }
+
+    const int* bt = a.block_table + (size_t)b * a.max_pages;
+    const int page_mask = (1 << a.page_shift) - 1;
+    const size_t tok_stride = PG == kDense ? (size_t)D : (size_t)a.Hkv * D;  // bytes between token rows
+    const size_t head_off = PG == kDense ? ((size_t)b * a.Hkv + g) * (size_t)a.max_kv_len * D : (size_t)g * D;
+
+    int pgv = 0;
+    if (PG == kPaged && lane < n_sl) pgv = bt[(T0 + stride * lane) >> a.page_shift];
+
+    const char* kbytes = static_cast<const char*>(a.k);
+    const char* vbytes = static_cast<const char*>(a.v);
+    const uint32_t* ssp = (lane & 16) ? a.v_ss : a.k_ss;  // lanes 0-15 K words, 16-31 V words
+    const int ss_tok = lane & 15;
+    auto issue = [&](int k) {
+        const int T = T0 + stride * k;
+        const uint32_t st = __builtin_amdgcn_readfirstlane(wlds_u + QB + (k & (NST - 1)) * STB);
+        const int last = hi - 1 - T;  // rows of the slice past `last` repeat row `last`
+        size_t row0;                  // byte offset of row T (head g)
+        if (PG == kPaged) {
+            const int page = k < 64 ? __builtin_amdgcn_readlane(pgv, k)
+                                    : ((const_int*)bt)[__builtin_amdgcn_readfirstlane(T >> a.page_shift)];
+            row0 = (((size_t)page << a.page_shift) + (size_t)(T & page_mask)) * tok_stride + head_off;
+        } else {
+            row0 = head_off + (size_t)T * D;
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const uint32_t voff = (uint32_t)(min(urow[i], last) * (int)tok_stride + lcol[i]);
+            dma16(kbytes + row0, voff, st + i * 1024);
+            dma16(vbytes + row0, voff, st + SLB + i * 1024);
+        }
+        // the scale-shift word of a (token row, head) sits at its byte offset / D
+        dma4(ssp + row0 / D + (size_t)min(ss_tok, last) * (tok_stride / D), st + 2 * SLB);
+    };
+
+    float m = -INFINITY, l = 0.f;
+    float pb = 0.f;  // sum over this lane's tokens of p_t * shift_t (V)
+    f32x4 acc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (n_sl > 0) {
+        // q rows of the head block (rows >= nh repeat the last head; zeroed below)
+        const int nqi = (nh + QRPI - 1) / QRPI;
+        for (int i = 0; i < nqi; ++i) {
+            const int qr = QRPI * i + lane / QCPR;
+            const int r = min(qr, nh - 1);
+            const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (qrow0 + r) * D +
+                                 (((lane % QCPR) ^ swz<D>(qr)) * 8);
+            dma16(qp, __builtin_amdgcn_readfirstlane(wlds_u + i * 1024));
+        }
+        const int pro = min(NST - 1, n_sl);
+        for (int k = 0; k < pro; ++k) issue(k);
+        wait_slices<PER_SLICE>(pro);
+
+        // q^T as the B operand (lane: head l % 16, dims 32 ks + 8 (l / 16)..+7) and sum_d q_d
+        const int hrow = lane & 15;
+        const int kq = lane >> 4;
+        u32x4 qop[KS];
+        float qsum = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const u32x4 x = lds16(wlds + hrow * QROWB + (((4 * ks + kq) ^ swz<D>(hrow)) << 4));
+            qop[ks] = hrow < nh ? x : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) qsum += pair_sum(TAG(), qop[ks][e]);
+        }
+        qsum += shfl_xor(qsum, 16);
+        qsum += xor32(qsum);
+        // LDS offsets: K operand (row l % 16, bytes 32 ks + 8 (l / 16)..+7), V
+        // conversion (row l / 4, quarter l % 4), transposed V reads
+        int koff[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            koff[ks] = hrow * KROWB + (((2 * ks + (kq >> 1)) ^ swz8<D>(hrow)) << 4) + 8 * (kq & 1);
+        const int vr = lane >> 2, vq = lane & 3;
+        int vsrc[SCH], vdst[2 * SCH];
+#pragma unroll
+        for (int j = 0; j < SCH; ++j) vsrc[j] = SLB + vr * KROWB + (((vq * SCH + j) ^ swz8<D>(vr)) << 4);
+#pragma unroll
+        for (int j = 0; j < 2 * SCH; ++j) vdst[j] = vr * QROWB + (((vq * 2 * SCH + j) ^ swz<D>(vr)) << 4);
+        int voff[NB];
+        {
+            const int j = lane & 15;
+            const int r = 4 * kq + (j >> 2);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int c = 2 * nb + ((j & 3) >> 1);
+                voff[nb] = r * QROWB + ((c ^ swz<D>(r)) << 4) + 8 * (j & 1);
+            }
+        }
+
+        for (int k = 0; k < n_sl; ++k) {
+            if (k + NST - 1 < n_sl) issue(k + NST - 1);
+            wait_slices<PER_SLICE>(min(NST - 1, n_sl - 1 - k));
+
+            const lds_char* st = wlds + QB + (k & (NST - 1)) * STB;
+            const u32x4 kw = lds16(st + 2 * SLB + 16 * kq);       // tokens 4 kq .. +3: K scale-shift
+            const u32x4 vw = lds16(st + 2 * SLB + 64 + 16 * kq);  // and V
+            f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const u32x2 x = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(st + koff[ks]);
+                const u32x2 lo8 = e4m3x4_to16(TAG(), x[0]), hi8 = e4m3x4_to16(TAG(), x[1]);
+                sc = mfma16x32(TAG(), u32x4{lo8[0], lo8[1], hi8[0], hi8[1]}, qop[ks], sc);
+            }
+            // this slice's V as 16-bit floats for the P.V product
+#pragma unroll
+            for (int j = 0; j < SCH; ++j) {
+                const u32x4 x = lds16(st + vsrc[j]);
+                const u32x2 a0 = e4m3x4_to16(TAG(), x[0]), a1 = e4m3x4_to16(TAG(), x[1]);
+                const u32x2 a2 = e4m3x4_to16(TAG(), x[2]), a3 = e4m3x4_to16(TAG(), x[3]);
+                *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(vcs + vdst[2 * j]) =
+                    u32x4{a0[0], a0[1], a1[0], a1[1]};
+                *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(vcs + vdst[2 * j + 1]) =
+                    u32x4{a2[0], a2[1], a3[0], a3[1]};
+            }
+            // dequantized scores: scale * (q . x) + shift * sum(q)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sc[r] = fmaf(sc[r], half_lo(kw[r]), half_hi(kw[r]) * qsum);
+
+            const int T = T0 + stride * k;
+            if (T + kSlice > hi) {  // ragged last slice of the chunk
+                const int tok = T + 4 * kq;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (tok + r >= hi) sc[r] = -INFINITY;
+            }
+            const float lm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])) * a.c;
+            if (__builtin_amdgcn_ballot_w64(lm > m + kRescaleLog2)) {
+                float mt = fmaxf(lm, shfl_xor(lm, 16));
+                mt = fmaxf(mt, xor32(mt));
+                const float mn = fmaxf(m, mt);
+                const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m - mn);
+                m = mn;
+                l *= alpha;
+                pb *= alpha;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float ar = lane_value(alpha, 4 * kq + r);  // acc row 4 (l/16) + r is head 4 (l/16) + r
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) acc[nb][r] *= ar;
+                }
+            }
+            const float mu = m == -INFINITY ? 0.f : m;
+            float p[4], pv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                p[r] = fast_exp2(fmaf(sc[r], a.c, -mu));
+                pv[r] = p[r] * half_lo(vw[r]);            // weight times the V row's scale
+                pb = fmaf(p[r], half_hi(vw[r]), pb);      // and the V row's shift
+            }
+            l += (p[0] + p[1]) + (p[2] + p[3]);
+            const u32x2 pop = {pack2(TAG(), pv[0], pv[1]), pack2(TAG(), pv[2], pv[3])};
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma16x16(TAG(), pop, lds_tr(vcs + voff[nb]), acc[nb]);
+        }
+    }
+
+    // ---- merge the NW waves' partial results -------------------------------
+    l += shfl_xor(l, 16);
+    l += xor32(l);
+    pb += shfl_xor(pb, 16);
+    pb += xor32(pb);
+    __syncthreads();  // every wave is done with its ring (and its loads have landed)
+    float* sacc = reinterpret_cast<float*>(smem_raw);  // [NW][16][D]
+    float* sm = sacc + NW * 16 * D;                    // [NW][16]
+    float* sl = sm + NW * 16;                          // [NW][16]
+    float* sp = sl + NW * 16;                          // [NW][16]
+    {
+        const int kq = lane >> 4, c = lane & 15;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sacc[(wave * 16 + 4 * kq + r) * D + 16 * nb + c] = acc[nb][r];
+        if (lane < 16) {
+            sm[wave * 16 + lane] = m;
+            sl[wave * 16 + lane] = l;
+            sp[wave * 16 + lane] = pb;
+        }
+    }
+    __syncthreads();
+    const size_t prow = qrow0 * a.n_splits + s;  // partial row of the block's first head
+    for (int i = tid; i < nh * D; i += NW * 64) {
+        const int h = i / D, d = i % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, sm[w * 16 + h]);
+        float L = 0.f, O = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float mw = sm[w * 16 + h];
+            const float e = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
+            L += e * sl[w * 16 + h];
+            O += e * (sacc[(w * 16 + h) * D + d] + sp[w * 16 + h]);
+        }
+        const size_t row = prow + (size_t)h * a.n_splits;
+        a.part_o[row * D + d] = L > 0.f ? O / L : 0.f;
+        if (d == 0) a.part_lse[row] = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
+    }
+}
+
 // One workgroup per query row (b, h, i): merge the non-empty chunks' partial
 // results.  Wave w merges the chunks s = w (mod 4) with weights relative to its
 // own maximum LSE (independent loads, eight at a time), and the four waves are
@@ -496,6 +830,27 @@ hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <class TAG, int D, int PG>
+hipError_t launch_split_fp8(const DecodeArgs& a, hipStream_t stream) {
+    const long long n_hb = (a.group + 15) / 16;
+    const long long blocks = (long long)a.B * a.Hkv * n_hb * a.n_splits;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((decode_split_kernel_fp8<TAG, D, DEC8_NW, DEC8_NST, PG>), dim3((unsigned)blocks),
+                       dim3(DEC8_NW * 64), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_combine_kernel<TAG, D>), dim3((unsigned)(a.B * a.Hq)), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <class TAG>
+hipError_t dispatch_fp8(const DecodeArgs& a, hipStream_t stream) {
+    const bool paged = a.block_table != nullptr;
+    if (a.D == 64)
+        return paged ? launch_split_fp8<TAG, 64, kPaged>(a, stream) : launch_split_fp8<TAG, 64, kDense>(a, stream);
+    return paged ? launch_split_fp8<TAG, 128, kPaged>(a, stream) : launch_split_fp8<TAG, 128, kDense>(a, stream);
+}
+
 template <class TAG, int D>
 hipError_t dispatch_layout(const DecodeArgs& a, hipStream_t stream) {
     if (a.block_table == nullptr) return launch_split<TAG, D, kDense>(a, stream);
@@ -514,6 +869,11 @@ hipError_t dispatch_d(const DecodeArgs& a, hipStream_t stream) {
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream) {
     if (dtype == kDtypeBF16) return dispatch_d<bf16_tag>(a, stream);
     return dispatch_d<f16_tag>(a, stream);
+}
+
+hipError_t launch_decode_fp8(const DecodeArgs& a, int dtype, hipStream_t stream) {
+    if (dtype == kDtypeBF16) return dispatch_fp8<bf16_tag>(a, stream);
+    return dispatch_fp8<f16_tag>(a, stream);
 }
 
 }  // namespace gqa

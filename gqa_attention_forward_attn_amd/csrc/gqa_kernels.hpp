@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace gqa {
 
@@ -55,6 +56,8 @@ struct DecodeArgs {
     float* part_lse;          // workspace [B, Hq, q_len, n_splits]
     int B, Hq, Hkv, D, group;
     int q_len;                // queries per sequence (1: plain decode)
+    const uint32_t* k_ss;     // E4M3 cache only: per (token row, K/V head) binary16 scale (bits 0-15)
+    const uint32_t* v_ss;     //   and shift (bits 16-31), laid out like the cache without D
     int max_pages;
     int page_shift;           // log2(page_size) (paged)
     int max_kv_len;           // dense row stride in tokens
@@ -63,5 +66,7 @@ struct DecodeArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream);
+// K/V as E4M3 bytes with scale-shift words (q_len = 1; pages of >= 16 tokens or dense).
+hipError_t launch_decode_fp8(const DecodeArgs& a, int dtype, hipStream_t stream);
 
 }  // namespace gqa

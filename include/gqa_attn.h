@@ -15,6 +15,10 @@
  *                       split along the keys and merged through the
  *                       per-chunk log-sum-exp (splitk_kernels.py,
  *                       `_fwd_kernel_splitK` and `_splitK_reduce`).
+ *   attn_decode_splitk_fp8
+ *                       the same over an 8-bit float (E4M3) KV cache with a
+ *                       binary16 scale and shift per token row and K/V head
+ *                       (the FP8_QUANTIZED case of `_fwd_kernel_splitK`).
  *   attn_decode_splitk_multi
  *                       the same with q_len queries per sequence at its last
  *                       positions, causal among themselves (the IS_CAUSAL /
@@ -181,6 +185,36 @@ gqa_status_t attn_decode_splitk(const void* q, const void* k, const void* v, voi
                                 float scale, int n_splits,
                                 void* workspace, size_t workspace_bytes,
                                 gqa_dtype_t dtype, void* hip_stream);
+
+/*
+ * attn_decode_splitk_fp8 - single-query split-K decode over an 8-bit float KV
+ * cache.  splitk_kernels.py, `_fwd_kernel_splitK` with FP8_QUANTIZED: every
+ * element of K and V is one OCP E4M3 byte (sign, 4-bit exponent with bias 7,
+ * 3-bit fraction, no infinities, S.1111.111 = NaN: the 8-bit float format of
+ * gfx950), and every (token row, K/V head) has a uint32 scale-shift word with a
+ * binary16 scale in bits 0-15 and a binary16 shift in bits 16-31
+ * (`cast_uint32_to_half2`).  The key / value used is byte * scale + shift
+ * (`dequantize`); the rest is attn_decode_splitk.
+ *
+ *   q, o        [B, Hq, D]   dtype (F16 or BF16)
+ *   lse         [B, Hq]      float32 (natural log)
+ *   k_cache, v_cache  uint8 E4M3, paged [num_pages, page_size, Hkv, D] with
+ *               block_table, or dense [B, Hkv, max_kv_len, D] without
+ *   k_scale_shift, v_scale_shift  uint32, [num_pages, page_size, Hkv] (paged)
+ *               or [B, Hkv, max_kv_len] (dense); 4-byte aligned
+ *   seq_lens, block_table, max_pages_per_seq, n_splits, workspace: as for
+ *               attn_decode_splitk (workspace >= attn_decode_workspace_bytes()).
+ *
+ * Requirements: those of attn_decode_splitk; a paged cache needs page_size >= 16
+ * (GQA_ERR_UNSUPPORTED otherwise).  The contents of the cache, the scale-shift
+ * words, seq_lens and block_table are trusted, as for attn_decode_splitk.
+ */
+gqa_status_t attn_decode_splitk_fp8(const void* q, const void* k_cache, const void* v_cache,
+                                    const uint32_t* k_scale_shift, const uint32_t* v_scale_shift,
+                                    void* o, float* lse, const int* seq_lens, const int* block_table,
+                                    int max_pages_per_seq, int page_size, int B, int Hq, int Hkv, int D,
+                                    int max_kv_len, float scale, int n_splits, void* workspace,
+                                    size_t workspace_bytes, gqa_dtype_t dtype, void* hip_stream);
 
 /*
  * attn_decode_workspace_bytes_multi - device workspace attn_decode_splitk_multi

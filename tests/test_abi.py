@@ -157,6 +157,27 @@ def test_prefill_paged_validation(L):
     assert pre_paged(L, max_q_len=0) == OK
 
 
+def dec_fp8(L, B=2, Hq=8, Hkv=2, D=128, max_kv_len=512, n_splits=4, page_size=256, max_pages=2,
+            bt=P[6], ws=P[7], ws_bytes=None, dtype=BF16, scale=0.1, q=P[0], seq=P[5], kss=P[1], vss=P[2]):
+    if ws_bytes is None:
+        ws_bytes = L.attn_decode_workspace_bytes(B, Hq, D, n_splits)
+    return L.attn_decode_splitk_fp8(q, P[1], P[2], kss, vss, P[3], P[4], seq, bt, max_pages, page_size,
+                                    B, Hq, Hkv, D, max_kv_len, scale, n_splits, ws, ws_bytes, dtype, None)
+
+
+def test_decode_fp8_validation(L):
+    assert dec_fp8(L, Hq=6, Hkv=4) == INVALID
+    assert dec_fp8(L, n_splits=0) == INVALID
+    assert dec_fp8(L, page_size=96) == INVALID
+    assert dec_fp8(L, page_size=8, max_pages=64) == UNSUPPORTED   # a page must hold a 16-token slice
+    assert dec_fp8(L, D=80) == UNSUPPORTED
+    assert dec_fp8(L, dtype=F32) == UNSUPPORTED
+    assert dec_fp8(L, kss=None) == INVALID
+    assert dec_fp8(L, vss=ctypes.c_void_p(0x20002)) == INVALID  # scale-shift words need 4-byte alignment
+    assert dec_fp8(L, ws=None) == WORKSPACE
+    assert dec_fp8(L, B=0) == OK
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     q = torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16)

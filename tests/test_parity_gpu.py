@@ -460,3 +460,109 @@ def test_prefill_paged_workload_sampled():
     e_o, e_l = check(o.reshape(-1, spec.D)[rows], l.reshape(-1)[rows], o_ref, l_ref, "bf16",
                      "ragged_paged_prefill")
     print(f"ragged_paged_prefill: {len(rows)} rows, max|dO|={e_o:.3e} max|dLSE|={e_l:.3e}")
+
+
+# ---- decode over an 8-bit E4M3 cache ----------------------------------------------
+
+def gpu_decode_fp8(inp, n_splits, scale, dense=None):
+    q = inp.q.cuda()
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full(q.shape[:2], float("nan"), dtype=torch.float32, device="cuda")
+    if dense is None:
+        o, l = gqa.attn_decode_splitk_fp8(q, inp.k8.cuda(), inp.v8.cuda(), inp.k_ss.cuda(), inp.v_ss.cuda(),
+                                          inp.seq_lens.cuda(), block_table=inp.block_table.cuda(),
+                                          n_splits=n_splits, scale=scale, max_kv_len=inp.max_kv_len,
+                                          out=out, lse=lse)
+    else:
+        k8, v8, kss, vss = (t.cuda() for t in dense)
+        o, l = gqa.attn_decode_splitk_fp8(q, k8, v8, kss, vss, inp.seq_lens.cuda(), n_splits=n_splits,
+                                          scale=scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return o.double().cpu().numpy(), l.double().cpu().numpy()
+
+
+def oracle_fp8(inp, scale, rows=None, dense=None):
+    if dense is None:
+        return oracle.attn_decode_fp8(inp.q, inp.k8, inp.v8, inp.k_ss, inp.v_ss, inp.seq_lens, scale,
+                                      block_table=inp.block_table, max_kv_len=inp.max_kv_len, rows=rows)
+    k8, v8, kss, vss = dense
+    return oracle.attn_decode_fp8(inp.q, k8, v8, kss, vss, inp.seq_lens, scale, rows=rows)
+
+
+def test_decode_fp8_workload_all_rows():
+    spec = W.FP8_PAGED_DECODE
+    print("workload fp8_paged_decode", flush=True)
+    inp = W.make_decode_fp8_spec(spec)
+    scale = W.fp32_scale(spec.D)
+    o, l = gpu_decode_fp8(inp, spec.n_splits, scale)
+    o_ref, l_ref = oracle_fp8(inp, scale)
+    e_o, e_l = check(o, l, o_ref, l_ref, "bf16", "fp8_paged_decode")
+    print(f"fp8_paged_decode: max|dO|={e_o:.3e} max|dLSE|={e_l:.3e}")
+
+
+DECODE_FP8 = [
+    # B, Hq, Hkv, D, dtype, len_lo, len_hi, page_size, n_splits
+    (4, 32, 8, 128, "bf16", 1, 700, 256, 16),
+    (3, 8, 8, 64, "f16", 1, 300, 16, 3),            # G = 1, 16-token pages
+    (2, 16, 2, 128, "bf16", 100, 2000, 64, 64),     # G = 8
+    (2, 6, 3, 64, "bf16", 500, 900, 128, 7),        # G = 2
+    (2, 32, 1, 128, "bf16", 100, 1500, 32, 8),      # G = 32: two blocks of 16 heads
+    (2, 20, 2, 64, "f16", 1, 400, 16, 5),           # G = 10
+]
+
+
+@pytest.mark.parametrize("case", DECODE_FP8, ids=lambda c: "-".join(map(str, c)))
+def test_decode_fp8_cases(case):
+    B, Hq, Hkv, D, dt, lo, hi, ps, ns = case
+    print(f"fp8 decode case {case}", flush=True)
+    inp = W.make_decode_fp8(B, Hq, Hkv, D, dt, seed=sum(case[:4]) + hi + 7, len_lo=lo, len_hi=hi, page_size=ps)
+    scale = W.fp32_scale(D)
+    o, l = gpu_decode_fp8(inp, ns, scale)
+    o_ref, l_ref = oracle_fp8(inp, scale)
+    check(o, l, o_ref, l_ref, dt, str(case))
+
+
+def test_decode_fp8_empty_and_short_sequences():
+    inp = W.make_decode_fp8(4, 8, 2, 128, "bf16", seed=70, seq_lens=[0, 1, 64, 65], page_size=64, max_pages=2)
+    inp.block_table[0, 0] = 0  # never read for an empty sequence
+    o, l = gpu_decode_fp8(inp, 16, 0.09)
+    o_ref, l_ref = oracle_fp8(inp, 0.09)
+    check(o, l, o_ref, l_ref, "bf16", "fp8 empty/short")
+    assert np.all(o[0] == 0) and np.all(np.isneginf(l[0]))
+
+
+def _fp8_dense(inp, Hkv, D):
+    B = inp.q.shape[0]
+    L = inp.max_kv_len
+    ps = inp.page_size
+    k8 = torch.zeros(B, Hkv, L, D, dtype=torch.uint8)
+    v8 = torch.zeros(B, Hkv, L, D, dtype=torch.uint8)
+    kss = torch.zeros(B, Hkv, L, dtype=torch.int32)
+    vss = torch.zeros(B, Hkv, L, dtype=torch.int32)
+    for b in range(B):
+        n = int(inp.seq_lens[b])
+        pages = inp.block_table[b, :(n + ps - 1) // ps].long()
+        k8[b, :, :n] = inp.k8[pages].reshape(-1, Hkv, D)[:n].permute(1, 0, 2)
+        v8[b, :, :n] = inp.v8[pages].reshape(-1, Hkv, D)[:n].permute(1, 0, 2)
+        kss[b, :, :n] = inp.k_ss[pages].reshape(-1, Hkv)[:n].permute(1, 0)
+        vss[b, :, :n] = inp.v_ss[pages].reshape(-1, Hkv)[:n].permute(1, 0)
+    return k8, v8, kss, vss
+
+
+def test_decode_fp8_dense_matches_paged_and_page_order():
+    kw = dict(B=3, Hq=8, Hkv=2, D=64, dtype="f16", seed=71, len_lo=10, len_hi=500, page_size=32)
+    a = W.make_decode_fp8(**kw, permute=True)
+    o1, l1 = gpu_decode_fp8(a, 4, 0.125)
+    dense = _fp8_dense(a, 2, 64)
+    o2, l2 = gpu_decode_fp8(a, 4, 0.125, dense=dense)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    o_ref, l_ref = oracle_fp8(a, 0.125, dense=dense)
+    check(o2, l2, o_ref, l_ref, "f16", "fp8 dense")
+    # the same logical cache with its pages in reverse order in the pool
+    n_pool = a.k8.shape[0]
+    b = W.DecodeFp8Inputs(a.q, a.k8.flip(0).contiguous(), a.v8.flip(0).contiguous(),
+                          a.k_ss.flip(0).contiguous(), a.v_ss.flip(0).contiguous(), a.seq_lens,
+                          torch.where(a.block_table >= 0, n_pool - 1 - a.block_table, a.block_table),
+                          a.page_size, a.max_kv_len)
+    o3, l3 = gpu_decode_fp8(b, 4, 0.125)
+    assert np.array_equal(o1, o3) and np.array_equal(l1, l3)
