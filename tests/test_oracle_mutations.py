@@ -26,9 +26,10 @@ MUTANTS = {
     "scale_dropped": ("s[t - lo] = scale * acc;", "s[t - lo] = acc;"),
     "max_not_subtracted": ("z += exp(s[t - lo] - m);", "z += exp(s[t - lo]);"),
     "prob_sign_flipped": ("double p = exp(s[t - lo] - L);", "double p = exp(L - s[t - lo]);"),
-    "values_read_from_keys": ("o[d] += p * elem(kv->v,", "o[d] += p * elem(kv->k,"),
-    "value_feature_shifted": ("o[d] += p * elem(kv->v, kv_index(kv, t, d), kv->dt);",
-                              "o[d] += p * elem(kv->v, kv_index(kv, t, (d + 1) % D), kv->dt);"),
+    "values_read_from_keys": ("o[d] += p * kv_value(kv, kv->v, kv->v_ss, t, d);",
+                              "o[d] += p * kv_value(kv, kv->k, kv->k_ss, t, d);"),
+    "value_feature_shifted": ("o[d] += p * kv_value(kv, kv->v, kv->v_ss, t, d);",
+                              "o[d] += p * kv_value(kv, kv->v, kv->v_ss, t, (d + 1) % D);"),
     "empty_row_lse_zero": ("*lse = -INFINITY;\n        return;", "*lse = 0.0;\n        return;"),
     "page_row_shifted": ("int64_t row = t % kv->page_size;", "int64_t row = (t + 1) % kv->page_size;"),
     "merge_weight_sign": ("double w = exp(ls[sp] - M);", "double w = exp(M - ls[sp]);"),
