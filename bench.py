@@ -319,8 +319,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build measures one GPU; run with --gpus 1 "
-                                   "(the multi-GPU sharding is described in DESIGN.md, not built)"}))
+        print(json.dumps({"error": "one GPU only: run with --gpus 1 (several GPUs would each run the "
+                                   "same kernels on their share; that sharding is not implemented)"}))
         sys.exit(2)
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
