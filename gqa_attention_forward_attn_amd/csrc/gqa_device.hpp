@@ -87,6 +87,44 @@ __device__ __forceinline__ uint32_t pack2(f16_tag, float a, float b) {
 }
 
 // Packed pair in the storage type -> two fp32 values.
+// One output row from the 32x32 MFMA accumulator with the queries as columns:
+// lane (q, half) holds dims 32 dt + 8 j + 4 half + 0..3 (j = 0..3) of row q.
+// A lane swap between the two 32-lane halves leaves each lane 16 consecutive
+// dims of every 32-dim block (half 0 the first 16), written scaled by inv as
+// two 16-byte stores: half the store instructions of 8-byte pieces, and 32
+// contiguous bytes of a row per lane pair.  Every lane of the wave executes
+// it (the swap reads the other half); `valid` masks the stores.
+template <class TAG, int DT>
+__device__ __forceinline__ void store_acc_row(TAG, const f32x16 (&acc)[DT], float inv, uint16_t* row, int half,
+                                              bool valid) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        uint32_t x[4][2];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[j][0] = pack2(TAG(), acc[dt][4 * j] * inv, acc[dt][4 * j + 1] * inv);
+            x[j][1] = pack2(TAG(), acc[dt][4 * j + 2] * inv, acc[dt][4 * j + 3] * inv);
+        }
+        // v_permlane32_swap: lanes 32-63 of the first operand trade places with
+        // lanes 0-31 of the second, so half 0 gets half 1's dims 4-7 (and
+        // 12-15) and half 1 gets half 0's dims 16-19 (and 24-27)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const auto r02 = __builtin_amdgcn_permlane32_swap(x[0][e], x[2][e], false, false);
+            const auto r13 = __builtin_amdgcn_permlane32_swap(x[1][e], x[3][e], false, false);
+            x[0][e] = r02[0];
+            x[2][e] = r02[1];
+            x[1][e] = r13[0];
+            x[3][e] = r13[1];
+        }
+        if (valid) {
+            uint16_t* dst = row + dt * 32 + half * 16;
+            *reinterpret_cast<u32x4*>(dst) = u32x4{x[0][0], x[0][1], x[2][0], x[2][1]};
+            *reinterpret_cast<u32x4*>(dst + 8) = u32x4{x[1][0], x[1][1], x[3][0], x[3][1]};
+        }
+    }
+}
+
 __device__ __forceinline__ float lo_to_f32(bf16_tag, uint32_t u) { return __builtin_bit_cast(float, u << 16); }
 __device__ __forceinline__ float hi_to_f32(bf16_tag, uint32_t u) { return __builtin_bit_cast(float, u & 0xffff0000u); }
 __device__ __forceinline__ float lo_to_f32(f16_tag, uint32_t u) {

@@ -382,20 +382,10 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
 
     // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----------------------------
     const float l_tot = l + xor32(l);
-    if (my_q < a.q_len) {
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        uint16_t* op = static_cast<uint16_t*>(a.o) + (q_head + my_q) * D;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int d0 = dt * 32 + 8 * r4 + 4 * half;
-                const u32x2 w = {pack2(TAG(), acc[dt][4 * r4] * inv, acc[dt][4 * r4 + 1] * inv),
-                                 pack2(TAG(), acc[dt][4 * r4 + 2] * inv, acc[dt][4 * r4 + 3] * inv)};
-                *reinterpret_cast<u32x2*>(op + d0) = w;
-            }
-        if (half == 0) a.lse[q_head + my_q] = l_tot > 0.f ? (m + fast_log2(l_tot)) * kLn2 : -INFINITY;
-    }
+    const bool valid = my_q < a.q_len;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    store_acc_row(TAG(), acc, inv, static_cast<uint16_t*>(a.o) + (q_head + min(my_q, a.q_len - 1)) * D, half, valid);
+    if (valid && half == 0) a.lse[q_head + my_q] = l_tot > 0.f ? (m + fast_log2(l_tot)) * kLn2 : -INFINITY;
 }
 
 template <class TAG, int D, bool CAUSAL, int NH>
