@@ -90,13 +90,12 @@ __device__ __forceinline__ uint32_t pack2(f16_tag, float a, float b) {
 // One output row from the 32x32 MFMA accumulator with the queries as columns:
 // lane (q, half) holds dims 32 dt + 8 j + 4 half + 0..3 (j = 0..3) of row q.
 // A lane swap between the two 32-lane halves leaves each lane 16 consecutive
-// dims of every 32-dim block (half 0 the first 16), written scaled by inv as
-// two 16-byte stores: half the store instructions of 8-byte pieces, and 32
-// contiguous bytes of a row per lane pair.  Every lane of the wave executes
-// it (the swap reads the other half); `valid` masks the stores.
+// dims of every 32-dim block (half 0 the first 16), scaled by inv and packed:
+// chunk 2 dt + e (e = 0, 1) holds dims 32 dt + 16 half + 8 e .. + 7, i.e. the
+// 16-byte chunk 4 dt + 2 half + e of the row.  Every lane of the wave must
+// execute it (the swap reads the other half).
 template <class TAG, int DT>
-__device__ __forceinline__ void store_acc_row(TAG, const f32x16 (&acc)[DT], float inv, uint16_t* row, int half,
-                                              bool valid) {
+__device__ __forceinline__ void acc_row_chunks(TAG, const f32x16 (&acc)[DT], float inv, u32x4 (&chunk)[2 * DT]) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
         uint32_t x[4][2];
@@ -117,10 +116,24 @@ __device__ __forceinline__ void store_acc_row(TAG, const f32x16 (&acc)[DT], floa
             x[1][e] = r13[0];
             x[3][e] = r13[1];
         }
-        if (valid) {
+        chunk[2 * dt] = u32x4{x[0][0], x[0][1], x[2][0], x[2][1]};
+        chunk[2 * dt + 1] = u32x4{x[1][0], x[1][1], x[3][0], x[3][1]};
+    }
+}
+
+// The same row written straight to global memory: two 16-byte stores per
+// 32-dim block (32 contiguous bytes of the row per lane pair).
+template <class TAG, int DT>
+__device__ __forceinline__ void store_acc_row(TAG, const f32x16 (&acc)[DT], float inv, uint16_t* row, int half,
+                                              bool valid) {
+    u32x4 chunk[2 * DT];
+    acc_row_chunks(TAG(), acc, inv, chunk);
+    if (valid) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
             uint16_t* dst = row + dt * 32 + half * 16;
-            *reinterpret_cast<u32x4*>(dst) = u32x4{x[0][0], x[0][1], x[2][0], x[2][1]};
-            *reinterpret_cast<u32x4*>(dst + 8) = u32x4{x[1][0], x[1][1], x[3][0], x[3][1]};
+            *reinterpret_cast<u32x4*>(dst) = chunk[2 * dt];
+            *reinterpret_cast<u32x4*>(dst + 8) = chunk[2 * dt + 1];
         }
     }
 }

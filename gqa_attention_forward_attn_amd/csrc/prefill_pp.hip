@@ -381,11 +381,39 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
     }
 
     // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----------------------------
+    // The wave's 32 rows are consecutive in o.  They are staged in LDS and
+    // written as whole rows (a store instruction covers 64 / CPR full rows).
+    // Staging area: wave w uses 32 rows of stage (n_tiles + w / 4) % NST, which
+    // no wave reads any more (the last tile, still read by group 1's final
+    // P.V, sits in stage (n_tiles - 1) % NST) and no load writes (tiles past
+    // the last are never issued).  Each wave reads back only what it wrote.
     const float l_tot = l + xor32(l);
-    const bool valid = my_q < a.q_len;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    store_acc_row(TAG(), acc, inv, static_cast<uint16_t*>(a.o) + (q_head + min(my_q, a.q_len - 1)) * D, half, valid);
-    if (valid && half == 0) a.lse[q_head + my_q] = l_tot > 0.f ? (m + fast_log2(l_tot)) * kLn2 : -INFINITY;
+    {
+        u32x4 chunk[2 * DT];
+        acc_row_chunks(TAG(), acc, inv, chunk);
+        lds_char* ob = smem + ((n_tiles + wave / 4) % NST) * STAGEB + (wave % 4) * (32 * ROWB);
+        // 16-byte chunk c of row r sits at chunk position c ^ oswz(r): conflict-free
+        // for both the row-per-lane writes and the chunk-per-lane reads
+        auto oswz = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
+#pragma unroll
+        for (int j = 0; j < 2 * DT; ++j) {
+            const int c = 4 * (j >> 1) + 2 * half + (j & 1);
+            *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(ob + l32 * ROWB + ((c ^ oswz(l32)) << 4)) =
+                chunk[j];
+        }
+        constexpr int RPI = 64 / CPR;  // rows per store instruction
+        char* og = reinterpret_cast<char*>(static_cast<uint16_t*>(a.o) + (q_head + pos0) * D);
+        const int cc = lane % CPR;
+#pragma unroll
+        for (int k = 0; k < 32 / RPI; ++k) {
+            const int rr = RPI * k + lane / CPR;
+            const u32x4 v =
+                *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(ob + rr * ROWB + ((cc ^ oswz(rr)) << 4));
+            if (pos0 + rr < a.q_len) *reinterpret_cast<u32x4*>(og + rr * ROWB + cc * 16) = v;
+        }
+    }
+    if (my_q < a.q_len && half == 0) a.lse[q_head + my_q] = l_tot > 0.f ? (m + fast_log2(l_tot)) * kLn2 : -INFINITY;
 }
 
 template <class TAG, int D, bool CAUSAL, int NH>
