@@ -44,8 +44,8 @@ METRIC = "attention fwd TFLOP/s + % bf16 MFMA peak; decode GB/s + % HBM peak"
 # other source reports traffic null.
 TRAFFIC_MEASUREMENT = {
     "source": "gqa_attention_forward_attn_amd/csrc/prefill_pp.hip",
-    "sha1": "10d9af1d78f1b811d6f57850b408abbc62687ea9",
-    "fetch_kib": 26835.2, "write_kib": 33280.0,
+    "sha1": "80eace581d781567a6bf6652d52624450f6dcf29",
+    "fetch_kib": 26624.2, "write_kib": 33280.0,
     "copy_fetch_kib": 262156.0, "copy_write_kib": 524288.0,
 }
 
