@@ -23,7 +23,8 @@ STATUS = {0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_UNSUPPORTED",
 _TORCH_DT = {torch.float32: GQA_F32, torch.float16: GQA_F16, torch.bfloat16: GQA_BF16}
 
 # Every symbol include/gqa_attn.h declares.
-EXPORTS = ("attn_fwd", "attn_prefill_paged", "attn_decode_workspace_bytes", "attn_decode_splitk",
+EXPORTS = ("attn_fwd", "attn_fwd_split", "attn_fwd_split_workspace_bytes", "attn_fwd_kv_splits",
+           "attn_prefill_paged", "attn_decode_workspace_bytes", "attn_decode_splitk",
            "attn_decode_splitk_fp8",
            "attn_decode_workspace_bytes_multi", "attn_decode_splitk_multi", "attn_status_str")
 
@@ -48,6 +49,12 @@ def lib() -> ctypes.CDLL:
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32, vp]
     L.attn_fwd.restype = i32
+    L.attn_fwd_split.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32, vp, sz, i32, vp]
+    L.attn_fwd_split.restype = i32
+    L.attn_fwd_split_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.attn_fwd_split_workspace_bytes.restype = sz
+    L.attn_fwd_kv_splits.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
+    L.attn_fwd_kv_splits.restype = i32
     L.attn_prefill_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                      f32, i32, i32, vp]
     L.attn_prefill_paged.restype = i32
@@ -89,11 +96,13 @@ def default_scale(D: int) -> float:
 
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
              scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-             lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+             lse: Optional[torch.Tensor] = None, kv_splits: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Attention forward. q [B,Hq,q_len,D], k/v [B,Hkv,kv_len,D] on one GPU.
 
     Returns (o [B,Hq,q_len,D] in q's dtype, lse [B,Hq,q_len] fp32, natural log).
     Causal masking is bottom-right aligned (query i sees keys j <= i + kv_len - q_len).
+    kv_splits: key ranges per block of query rows (attn_fwd_split); None lets the
+    library choose (attn_fwd_kv_splits), 1 forces the single-pass forward.
     """
     B, Hq, q_len, D = q.shape
     Bk, Hkv, kv_len, Dk = k.shape
@@ -109,8 +118,20 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = T
     if lse is None:
         lse = torch.empty((B, Hq, q_len), dtype=torch.float32, device=q.device)
     sc = default_scale(D) if scale is None else float(scale)
+    dt = _TORCH_DT[q.dtype]
+    if kv_splits is None:
+        kv_splits = int(lib().attn_fwd_kv_splits(B, Hq, Hkv, q_len, kv_len, D, int(bool(causal)), dt))
+    if kv_splits > 1:
+        # small grids: key ranges in parallel, merged by LSE (workspace from torch's allocator)
+        ws = torch.empty(int(lib().attn_fwd_split_workspace_bytes(B, Hq, q_len, D, kv_splits)),
+                         dtype=torch.uint8, device=q.device)
+        rc = lib().attn_fwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, q_len, kv_len, D,
+                                  sc, int(bool(causal)), int(kv_splits), _ptr(ws), ws.numel(), dt,
+                                  _stream(q.device))
+        _check("attn_fwd_split", rc)
+        return out, lse
     rc = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, q_len, kv_len, D,
-                        sc, int(bool(causal)), _TORCH_DT[q.dtype], _stream(q.device))
+                        sc, int(bool(causal)), dt, _stream(q.device))
     _check("attn_fwd", rc)
     return out, lse
 

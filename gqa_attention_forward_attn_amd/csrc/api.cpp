@@ -74,6 +74,67 @@ gqa_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, floa
     return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 
+int attn_fwd_kv_splits(int B, int Hq, int Hkv, int q_len, int kv_len, int D, int causal, gqa_dtype_t dtype) {
+    (void)causal;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || q_len <= 0 || kv_len <= 0 || Hq % Hkv != 0) return 1;
+    if (!supported_head_dim(D) || (dtype != GQA_BF16 && dtype != GQA_F16)) return 1;
+    // Only where the ping-pong kernel would leave at least half of the CUs idle,
+    // and only with enough keys that each range keeps a deep tile loop.
+    if (kv_len < 2048) return 1;
+    int dev = 0, n_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
+        return 1;
+    // as many ranges as fit one workgroup per CU (rounded down: a second round
+    // of workgroups costs more than the idle CUs it would fill)
+    const long long items = gqa::prefill_pp_items(B, Hq, Hkv, q_len);
+    long long splits = n_cu / items;
+    const long long max_by_keys = kv_len / 1024;  // at least 16 key tiles per range
+    if (splits > max_by_keys) splits = max_by_keys;
+    if (splits > 8) splits = 8;
+    return splits < 2 ? 1 : (int)splits;
+}
+
+size_t attn_fwd_split_workspace_bytes(int B, int Hq, int q_len, int D, int kv_splits) {
+    if (B <= 0 || Hq <= 0 || q_len <= 0 || D <= 0 || kv_splits <= 1) return 0;
+    return (size_t)B * Hq * q_len * kv_splits * (size_t)(D + 1) * sizeof(float);
+}
+
+gqa_status_t attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int Hq, int Hkv, int q_len, int kv_len, int D, float scale, int causal,
+                            int kv_splits, void* workspace, size_t workspace_bytes, gqa_dtype_t dtype,
+                            void* hip_stream) {
+    if (kv_splits < 1) return GQA_ERR_INVALID_ARG;
+    if (kv_splits == 1 || kv_len == 0)
+        return attn_fwd(q, k, v, o, lse, B, Hq, Hkv, q_len, kv_len, D, scale, causal, dtype, hip_stream);
+    if (B < 0 || q_len < 0 || kv_len < 0 || Hq <= 0 || Hkv <= 0 || D <= 0) return GQA_ERR_INVALID_ARG;
+    if (Hq % Hkv != 0) return GQA_ERR_INVALID_ARG;
+    if (!valid_dtype(dtype)) return GQA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return GQA_ERR_INVALID_ARG;
+    if (!supported_head_dim(D) || dtype == GQA_F32) return GQA_ERR_UNSUPPORTED;
+    if (B == 0 || q_len == 0) return GQA_OK;
+    if (!q || !k || !v || !o || !lse) return GQA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(o) || !aligned16(k) || !aligned16(v)) return GQA_ERR_INVALID_ARG;
+    const long long rows_q = (long long)B * Hq * q_len;
+    const long long rows_kv = (long long)B * Hkv * kv_len;
+    if (rows_q > (1LL << 40) || rows_kv > (1LL << 40) || kv_splits > 64) return GQA_ERR_INVALID_ARG;
+    const size_t need = attn_fwd_split_workspace_bytes(B, Hq, q_len, D, kv_splits);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return GQA_ERR_WORKSPACE;
+
+    gqa::PrefillArgs a{};
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.q_len = q_len; a.kv_len = kv_len;
+    a.group = Hq / Hkv;
+    a.delta = kv_len - q_len;
+    a.c = scale * kLog2e;
+    a.kv_splits = kv_splits;
+    a.part_o = static_cast<float*>(workspace);
+    a.part_lse = a.part_o + (size_t)rows_q * kv_splits * D;
+    hipError_t e = gqa::launch_prefill_split(a, D, causal != 0, to_kernel_dtype(dtype),
+                                             static_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
 gqa_status_t attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
                                 const int* qo_indptr, const int* kv_indptr, const int* kv_indices,
                                 const int* kv_last_page_len, int B, int Hq, int Hkv, int D, int page_size,

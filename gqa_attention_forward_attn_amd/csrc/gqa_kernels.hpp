@@ -24,6 +24,13 @@ struct PrefillArgs {
     int n_pos_tiles;  // filled by the launcher
     int n_rest;       // filled by the launcher
     float c;          // scale * log2(e)
+    // Split-KV prefill (ping-pong kernel): the key tiles of every row block are
+    // cut into kv_splits ranges; range s writes O_s (fp32) and its natural-base
+    // LSE_s to part_o [B, Hq, q_len, kv_splits, D] / part_lse [B, Hq, q_len,
+    // kv_splits], merged afterwards.  kv_splits = 1: the plain forward.
+    int kv_splits;
+    float* part_o;
+    float* part_lse;
     // Ragged batch over a paged cache (paged prefill only): q, o token-major
     // [total_q, Hq, D], lse [total_q, Hq]; k, v [num_pages, page_size, Hkv, D].
     // q_len holds the largest per-request query count (sizes the grid).
@@ -43,6 +50,11 @@ hipError_t launch_prefill(PrefillArgs a, int D, bool causal, int dtype, PrefillK
 hipError_t launch_prefill_paged(PrefillArgs a, int D, bool causal, int dtype, hipStream_t stream);
 // Ping-pong schedule, 8 waves x 32 rows (bf16 / fp16 only).
 hipError_t launch_prefill_pp(PrefillArgs a, int D, bool causal, int dtype, hipStream_t stream);
+// Split-KV prefill on the ping-pong kernel (a.kv_splits > 1 with part_o / part_lse
+// set), then the merge into o / lse.
+hipError_t launch_prefill_split(PrefillArgs a, int D, bool causal, int dtype, hipStream_t stream);
+// Workgroups of the ping-pong kernel for this shape (one per 256 (query, head) rows).
+long long prefill_pp_items(int B, int Hq, int Hkv, int q_len);
 
 struct DecodeArgs {
     const void* q;            // [B, Hq, q_len, D]

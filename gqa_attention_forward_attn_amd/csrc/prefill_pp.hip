@@ -122,8 +122,15 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
     const int l32 = lane & 31;
 
     // ---- work item ----------------------------------------------------------
-    int pt = blockIdx.x / a.n_rest;
-    int rest = blockIdx.x - pt * a.n_rest;
+    // (position tile, head block, kv head, batch[, key range]), key range fastest
+    int id = blockIdx.x;
+    int split = 0;
+    if (a.kv_splits > 1) {
+        split = id % a.kv_splits;
+        id /= a.kv_splits;
+    }
+    int pt = id / a.n_rest;
+    int rest = id - pt * a.n_rest;
     if (CAUSAL) pt = a.n_pos_tiles - 1 - pt;  // longest rows first
     const int hgroups = a.group / NH;
     const int hg = rest % hgroups;
@@ -141,8 +148,14 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
         wg_kv_end = max(0, min(a.kv_len, wg_last + a.delta + 1));
         wave_full_end = max(0, min(a.kv_len, pos0 + a.delta + 1));
     }
-    const int n_tiles = (wg_kv_end + BN - 1) / BN;
-    const int n_full = min(wave_full_end / BN, n_tiles);
+    // this workgroup's key tiles t_lo .. t_lo + n_tiles - 1 (all of them unless
+    // the keys are split); loop indices below are relative to t_lo
+    const int n_all = (wg_kv_end + BN - 1) / BN;
+    const int n_split = a.kv_splits > 1 ? a.kv_splits : 1;
+    const int per_split = (n_all + n_split - 1) / n_split;
+    const int t_lo = min(n_all, split * per_split);
+    const int n_tiles = min(n_all, t_lo + per_split) - t_lo;
+    const int n_full = min(wave_full_end / BN, n_all) - t_lo;  // relative tiles below it need no mask
     const int lim = CAUSAL ? min(my_q + a.delta + 1, a.kv_len) : a.kv_len;  // keys < lim are visible
 
     // ---- Q (B operand of S^T = K Q^T) ---------------------------------------
@@ -171,7 +184,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
         ld_col[j] = (pc ^ swz<D>(row)) * 16;
     }
     auto issue_tile = [&](int t) {
-        const int t0 = t * BN;
+        const int t0 = (t_lo + t) * BN;
         lds_char* st = smem + (t % NST) * STAGEB;
 #pragma unroll
         for (int j = 0; j < LPW; ++j) {
@@ -298,7 +311,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
     // VALU phase of tile t: mask, row max, lazy rescale, weights
     auto valu_phase = [&](int t) {
         if (t >= n_full) {  // diagonal / tail tile
-            const int k0 = t * BN;
+            const int k0 = (t_lo + t) * BN;
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
@@ -389,6 +402,23 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
     // the last are never issued).  Each wave reads back only what it wrote.
     const float l_tot = l + xor32(l);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (a.kv_splits > 1) {
+        // partial result of this key range: O_s = acc / l (0 when none of its
+        // keys is visible to the row) and LSE_s (-inf then), both fp32
+        if (my_q < a.q_len) {
+            const size_t prow = (q_head + my_q) * a.kv_splits + split;
+            float* po = a.part_o + prow * D;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4)
+                    *reinterpret_cast<f32x4*>(po + dt * 32 + 8 * r4 + 4 * half) =
+                        f32x4{acc[dt][4 * r4] * inv, acc[dt][4 * r4 + 1] * inv, acc[dt][4 * r4 + 2] * inv,
+                              acc[dt][4 * r4 + 3] * inv};
+            if (half == 0) a.part_lse[prow] = l_tot > 0.f ? (m + fast_log2(l_tot)) * kLn2 : -INFINITY;
+        }
+        return;
+    }
     {
         u32x4 chunk[2 * DT];
         acc_row_chunks(TAG(), acc, inv, chunk);
@@ -416,14 +446,60 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
     if (my_q < a.q_len && half == 0) a.lse[q_head + my_q] = l_tot > 0.f ? (m + fast_log2(l_tot)) * kLn2 : -INFINITY;
 }
 
+// Merge of the key ranges of a split-KV prefill, the LSE merge of the split-K
+// decode (splitk_kernels.py, `_splitK_reduce`): per query row, M = max_s LSE_s,
+// w_s = exp(LSE_s - M), O = sum w_s O_s / sum w_s, LSE = M + log(sum w_s); a row
+// with no visible key in any range gives (0, -inf).  One thread per 8 output
+// dims of a row.
+template <class TAG, int D>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a, long long rows) {
+    constexpr int G = D / 8;
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= rows * G) return;
+    const long long row = i / G;
+    const int d0 = (int)(i - row * G) * 8;
+    const int S = a.kv_splits;
+    const float* pl = a.part_lse + row * S;
+    float M = -INFINITY;
+    for (int sp = 0; sp < S; ++sp) M = fmaxf(M, pl[sp]);
+    float W = 0.f, O[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) O[e] = 0.f;
+    for (int sp = 0; sp < S; ++sp) {
+        const float lv = pl[sp];
+        if (lv == -INFINITY) continue;
+        const float w = fast_exp2((lv - M) * kLog2e);
+        W += w;
+        const float* po = a.part_o + (row * S + sp) * D + d0;
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(po);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(po + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            O[e] += w * x0[e];
+            O[4 + e] += w * x1[e];
+        }
+    }
+    const float inv = W > 0.f ? 1.f / W : 0.f;
+    const u32x4 packed = {pack2(TAG(), O[0] * inv, O[1] * inv), pack2(TAG(), O[2] * inv, O[3] * inv),
+                          pack2(TAG(), O[4] * inv, O[5] * inv), pack2(TAG(), O[6] * inv, O[7] * inv)};
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.o) + row * D + d0) = packed;
+    if (d0 == 0) a.lse[row] = W > 0.f ? M + fast_log2(W) * kLn2 : -INFINITY;
+}
+
 template <class TAG, int D, bool CAUSAL, int NH>
 hipError_t launch_pp(PrefillArgs a, hipStream_t stream) {
     constexpr int POS = 256 / NH;
     a.n_pos_tiles = (a.q_len + POS - 1) / POS;
     a.n_rest = a.B * a.Hkv * (a.group / NH);
-    const long long blocks = (long long)a.n_pos_tiles * a.n_rest;
+    const long long blocks = (long long)a.n_pos_tiles * a.n_rest * (a.kv_splits > 1 ? a.kv_splits : 1);
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((prefill_fwd_pp<TAG, D, CAUSAL, NH>), dim3((unsigned)blocks), dim3(512), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.kv_splits <= 1) return e;
+    const long long rows = (long long)a.B * a.Hq * a.q_len;
+    const long long merge_blocks = (rows * (D / 8) + 255) / 256;
+    if (merge_blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((prefill_merge_kernel<TAG, D>), dim3((unsigned)merge_blocks), dim3(256), 0, stream, a, rows);
     return hipGetLastError();
 }
 
@@ -442,6 +518,17 @@ hipError_t dispatch_d(PrefillArgs a, int D, bool causal, hipStream_t stream) {
 }
 
 }  // namespace
+
+long long prefill_pp_items(int B, int Hq, int Hkv, int q_len) {
+    const int group = Hq / Hkv;
+    const int nh = group % 8 == 0 ? 8 : group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
+    const int pos = 256 / nh;
+    return (long long)B * Hkv * (group / nh) * ((q_len + pos - 1) / pos);
+}
+
+hipError_t launch_prefill_split(PrefillArgs a, int D, bool causal, int dtype, hipStream_t stream) {
+    return launch_prefill_pp(a, D, causal, dtype, stream);
+}
 
 hipError_t launch_prefill_pp(PrefillArgs a, int D, bool causal, int dtype, hipStream_t stream) {
     if (dtype == kDtypeBF16) return dispatch_d<bf16_tag>(a, D, causal, stream);

@@ -5,6 +5,7 @@
  * query heads:
  *
  *   attn_fwd            prefill / general forward, FlashAttention style
+ *   attn_fwd_split      the same with the keys split into ranges and merged (small grids)
  *                       (causal_forward_kernel.py, `_flash_attention_forward_gqa_kernel`
  *                       and its wrapper `flash_attention_forward`).
  *   attn_prefill_paged  the same forward for a batch of ragged requests whose
@@ -96,6 +97,48 @@ typedef enum {
 gqa_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                       int B, int Hq, int Hkv, int q_len, int kv_len, int D,
                       float scale, int causal, gqa_dtype_t dtype, void* hip_stream);
+
+/*
+ * attn_fwd_split - the same forward with the keys of every block of query rows
+ * cut into kv_splits contiguous ranges processed in parallel, then merged: the
+ * split-K partition and LSE merge of splitk_kernels.py (`_fwd_kernel_splitK`
+ * writes a partial output and its LSE per key range, `_splitK_reduce` merges
+ * them: M = max_s LSE_s, w_s = exp(LSE_s - M), O = sum w_s O_s / sum w_s,
+ * LSE = M + log sum w_s), applied to prefill so that shapes with fewer blocks
+ * of query rows than compute units still fill the chip.
+ *
+ * Arguments and results as attn_fwd (results equal up to rounding order),
+ * plus:
+ *   kv_splits  >= 1 key ranges per block of rows (1: exactly attn_fwd;
+ *              at most 64).  Ranges hold whole 64-key tiles; a range can be
+ *              empty, and a row that sees no key of a range gives it
+ *              (O_s, LSE_s) = (0, -inf).
+ *   workspace  device memory owned by the caller, 16-byte aligned, at least
+ *              attn_fwd_split_workspace_bytes(B, Hq, q_len, D, kv_splits) bytes
+ *              (fp32 partial outputs [B, Hq, q_len, kv_splits, D], then fp32
+ *              partial LSEs [B, Hq, q_len, kv_splits]); its contents on entry
+ *              do not matter and are undefined afterwards.  Unused when
+ *              kv_splits == 1 (may be NULL).
+ * dtype F16 or BF16 when kv_splits > 1 (F32: GQA_ERR_UNSUPPORTED).
+ * Returns GQA_ERR_WORKSPACE when the workspace is missing, misaligned or too
+ * small, otherwise as attn_fwd.  Two launches on hip_stream (ranges, merge).
+ */
+size_t attn_fwd_split_workspace_bytes(int B, int Hq, int q_len, int D, int kv_splits);
+gqa_status_t attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int Hq, int Hkv, int q_len, int kv_len, int D, float scale, int causal,
+                            int kv_splits, void* workspace, size_t workspace_bytes, gqa_dtype_t dtype,
+                            void* hip_stream);
+
+/*
+ * attn_fwd_kv_splits - the key-range count the library recommends for
+ * attn_fwd_split on this shape on the current device: for F16/BF16 with
+ * kv_len >= 2048, as many ranges as fit one workgroup of 256 (query, head) rows
+ * per compute unit (CU count / blocks of rows, rounded down; at most
+ * kv_len / 1024 so that each range keeps >= 16 key tiles, at most 8); 1 when
+ * that is 1 or the shape does not qualify (call attn_fwd).  Host-only; reads
+ * the device's CU count.
+ */
+int attn_fwd_kv_splits(int B, int Hq, int Hkv, int q_len, int kv_len, int D, int causal, gqa_dtype_t dtype);
 
 /*
  * attn_prefill_paged - attention forward for a batch of B ragged requests over

@@ -77,6 +77,44 @@ def test_fwd_validation(L):
     assert fwd(L, q_len=0) == OK
 
 
+def fwd_split(L, kv_splits=2, ws=P[7], ws_bytes=None, B=1, Hq=4, Hkv=2, q_len=8, kv_len=8, D=64, dtype=BF16,
+              q=P[0]):
+    if ws_bytes is None:
+        ws_bytes = L.attn_fwd_split_workspace_bytes(B, Hq, q_len, D, kv_splits)
+    return L.attn_fwd_split(q, P[1], P[2], P[3], P[4], B, Hq, Hkv, q_len, kv_len, D, 0.125, 1, kv_splits,
+                            ws, ws_bytes, dtype, None)
+
+
+def test_fwd_split_workspace_and_validation(L):
+    # fp32 partial outputs [B, Hq, q_len, kv_splits, D] then partial LSEs
+    assert L.attn_fwd_split_workspace_bytes(1, 32, 1024, 128, 2) == 32 * 1024 * 2 * 129 * 4
+    assert L.attn_fwd_split_workspace_bytes(1, 32, 1024, 128, 1) == 0
+    assert L.attn_fwd_split_workspace_bytes(0, 32, 1024, 128, 2) == 0
+    assert fwd_split(L, kv_splits=0) == INVALID
+    assert fwd_split(L, kv_splits=65) == INVALID
+    assert fwd_split(L, Hq=6, Hkv=4) == INVALID
+    assert fwd_split(L, D=96) == UNSUPPORTED
+    assert fwd_split(L, dtype=F32) == UNSUPPORTED
+    assert fwd_split(L, ws=None) == WORKSPACE
+    assert fwd_split(L, ws_bytes=16) == WORKSPACE
+    assert fwd_split(L, ws=ctypes.c_void_p(0x20008)) == WORKSPACE   # misaligned
+    assert fwd_split(L, q=None) == INVALID
+    assert fwd_split(L, B=0) == OK
+    # kv_splits = 1 is attn_fwd itself (no workspace needed)
+    assert fwd_split(L, kv_splits=1, ws=None, ws_bytes=0, B=0) == OK
+    assert fwd_split(L, kv_splits=1, ws=None, ws_bytes=0, Hq=6, Hkv=4) == INVALID
+
+
+def test_fwd_kv_splits_recommendation(L):
+    # never for fp32, short key ranges or bad geometry; without a device (host
+    # only) the CU count is unknown and the answer is 1
+    assert L.attn_fwd_kv_splits(1, 32, 4, 1024, 4096, 128, 1, F32) == 1
+    assert L.attn_fwd_kv_splits(1, 32, 4, 1024, 1024, 128, 1, BF16) == 1
+    assert L.attn_fwd_kv_splits(1, 6, 4, 1024, 4096, 128, 1, BF16) == 1
+    assert L.attn_fwd_kv_splits(1, 32, 4, 1024, 4096, 96, 1, BF16) == 1
+    assert L.attn_fwd_kv_splits(1, 32, 4, 1024, 4096, 128, 1, BF16) >= 1
+
+
 def dec(L, B=2, Hq=8, Hkv=2, D=128, max_kv_len=512, n_splits=4, page_size=256, max_pages=2,
         bt=P[6], ws=P[7], ws_bytes=None, dtype=BF16, scale=0.1, q=P[0], seq=P[5]):
     if ws_bytes is None:

@@ -35,11 +35,11 @@ def check(o_gpu, lse_gpu, o_ref, lse_ref, dtname, what=""):
     return err_o, err_l
 
 
-def gpu_fwd(q, k, v, causal, scale, canary=True):
+def gpu_fwd(q, k, v, causal, scale, canary=True, kv_splits=1):
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     out = torch.full_like(qd, float("nan")) if canary else None
     lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device="cuda") if canary else None
-    o, l = gqa.attn_fwd(qd, kd, vd, causal=causal, scale=scale, out=out, lse=lse)
+    o, l = gqa.attn_fwd(qd, kd, vd, causal=causal, scale=scale, out=out, lse=lse, kv_splits=kv_splits)
     torch.cuda.synchronize()
     return o, l
 
@@ -80,6 +80,42 @@ def test_prefill_all_elements(shape, kernel, monkeypatch):
     check(o.double().cpu().numpy(), l.double().cpu().numpy(), o_ref, l_ref, dt, str(shape))
 
 
+# ---- split-KV prefill: key ranges in parallel, merged by LSE ----------------
+
+SPLIT = [
+    # B, Hq, Hkv, q_len, kv_len, D, dtype, causal, kv_splits
+    (1, 8, 2, 200, 700, 128, "bf16", True, 2),
+    (1, 8, 2, 200, 700, 128, "bf16", True, 3),
+    (2, 4, 4, 130, 333, 64, "f16", False, 2),
+    (2, 4, 4, 130, 333, 64, "f16", False, 5),
+    (1, 32, 4, 96, 2100, 128, "bf16", True, 4),     # bottom-right offset, G = 8
+    (2, 4, 2, 300, 100, 64, "bf16", True, 3),       # q_len > kv_len: leading rows see no key
+    (1, 6, 3, 257, 257, 128, "f16", True, 8),       # more ranges than some row blocks have tiles
+    (1, 12, 4, 64, 64, 64, "bf16", True, 2),        # G = 3, a single key tile
+]
+
+
+@pytest.mark.parametrize("case", SPLIT, ids=lambda c: "-".join(map(str, c)))
+def test_prefill_split_all_elements(case, monkeypatch):
+    B, Hq, Hkv, Lq, Lk, D, dt, causal, S = case
+    print(f"split prefill case {case}", flush=True)
+    q, k, v = W.make_prefill(B, Hq, Hkv, Lq, Lk, D, dt, seed=sum(case[:6]) + S)
+    scale = W.fp32_scale(D)
+    o, l = gpu_fwd(q, k, v, causal, scale, kv_splits=S)
+    o_ref, l_ref = oracle.attn_fwd(q, k, v, scale, causal)
+    check(o.double().cpu().numpy(), l.double().cpu().numpy(), o_ref, l_ref, dt, str(case))
+    # the merge of the ranges equals the single pass of the same kernel up to
+    # rounding: the tiles and their rounded weights are the same, only the
+    # order of the fp32 sums and the final rounding differ
+    monkeypatch.setenv("GQA_ATTN_PREFILL_KERNEL", "pingpong")
+    o1, l1 = gpu_fwd(q, k, v, causal, scale, kv_splits=1)
+    lf, l1f = l.cpu(), l1.cpu()
+    assert torch.equal(torch.isneginf(lf), torch.isneginf(l1f))
+    fin = torch.isfinite(l1f)
+    assert float((lf[fin] - l1f[fin]).abs().max()) <= 1e-5
+    assert float((o.float() - o1.float()).abs().max()) <= 1.6e-2
+
+
 def test_prefill_kv_len_zero():
     q = torch.randn(1, 4, 16, 64).to(torch.bfloat16)
     k = torch.zeros(1, 2, 0, 64, dtype=torch.bfloat16)
@@ -105,17 +141,24 @@ def sample_rows(B, Hq, Lq, n_random, seed):
 
 
 WORKLOAD_CASES = [(s, kern) for s in W.PREFILL_WORKLOADS
-                  for kern in (PREFILL_KERNELS if s.dtype != "f32" else ["auto"])]
+                  for kern in (PREFILL_KERNELS + ["split"] if s.dtype != "f32" else ["auto"])]
 
 
 @pytest.mark.parametrize("spec,kernel", WORKLOAD_CASES,
                          ids=lambda c: c.name if hasattr(c, "name") else c)
 def test_prefill_workload_sampled(spec, kernel, monkeypatch):
-    monkeypatch.setenv("GQA_ATTN_PREFILL_KERNEL", kernel)
-    print(f"workload {spec.name} kernel {kernel}", flush=True)
+    # "split": key ranges merged by LSE, with the library's range count for the
+    # shape (at least 2, so that every workload also runs the split path)
+    splits = 1
+    if kernel == "split":
+        splits = max(2, gqa.lib().attn_fwd_kv_splits(spec.B, spec.Hq, spec.Hkv, spec.q_len, spec.kv_len,
+                                                     spec.D, int(spec.causal), gqa._TORCH_DT[W._DTYPES[spec.dtype]]))
+    else:
+        monkeypatch.setenv("GQA_ATTN_PREFILL_KERNEL", kernel)
+    print(f"workload {spec.name} kernel {kernel} kv_splits {splits}", flush=True)
     q, k, v = W.make_prefill_spec(spec)
     scale = W.fp32_scale(spec.D)
-    o, l = gpu_fwd(q, k, v, spec.causal, scale)
+    o, l = gpu_fwd(q, k, v, spec.causal, scale, kv_splits=splits)
     o = o.double().cpu().numpy().reshape(-1, spec.D)
     l = l.double().cpu().numpy().reshape(-1)
     # properties at every row: finite (every row here sees at least one key)
