@@ -44,8 +44,8 @@ METRIC = "attention fwd TFLOP/s + % bf16 MFMA peak; decode GB/s + % HBM peak"
 # other source reports traffic null.
 TRAFFIC_MEASUREMENT = {
     "source": "gqa_attention_forward_attn_amd/csrc/prefill_pp.hip",
-    "sha1": "80eace581d781567a6bf6652d52624450f6dcf29",
-    "fetch_kib": 26624.2, "write_kib": 33280.0,
+    "sha1": "60f3dbfd7ab2b1716d739732db2cb60073b04490",
+    "fetch_kib": 26597.6, "write_kib": 33280.0,
     "copy_fetch_kib": 262156.0, "copy_write_kib": 524288.0,
 }
 
