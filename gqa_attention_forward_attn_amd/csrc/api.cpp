@@ -165,7 +165,7 @@ gqa_status_t attn_prefill_paged(const void* q, const void* k_cache, const void* 
     a.kv_indices = kv_indices;
     a.kv_last_page_len = kv_last_page_len;
     a.page_shift = page_shift;
-    hipError_t e = gqa::launch_prefill_paged(a, D, causal != 0, to_kernel_dtype(dtype),
+    hipError_t e = gqa::launch_prefill_paged(a, D, causal != 0, to_kernel_dtype(dtype), prefill_kernel_choice(),
                                              static_cast<hipStream_t>(hip_stream));
     return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }

@@ -46,8 +46,12 @@ enum class PrefillKernel { kAuto, kPingPong, kFourWave };
 
 // Validated arguments only.  D in {64, 128}; dtype one of kDtype*.
 hipError_t launch_prefill(PrefillArgs a, int D, bool causal, int dtype, PrefillKernel kernel, hipStream_t stream);
-// Ragged batch of requests over a paged K/V cache (bf16 / fp16, four-wave kernel).
-hipError_t launch_prefill_paged(PrefillArgs a, int D, bool causal, int dtype, hipStream_t stream);
+// Ragged batch of requests over a paged K/V cache (bf16 / fp16): the ping-pong
+// kernel for batches that give every CU a workgroup, else the four-wave kernel
+// (or the one `kernel` forces).
+hipError_t launch_prefill_paged(PrefillArgs a, int D, bool causal, int dtype, PrefillKernel kernel, hipStream_t stream);
+// The ping-pong kernel's paged mode.
+hipError_t launch_prefill_pp_paged(PrefillArgs a, int D, bool causal, int dtype, hipStream_t stream);
 // Ping-pong schedule, 8 waves x 32 rows (bf16 / fp16 only).
 hipError_t launch_prefill_pp(PrefillArgs a, int D, bool causal, int dtype, hipStream_t stream);
 // Split-KV prefill on the ping-pong kernel (a.kv_splits > 1 with part_o / part_lse

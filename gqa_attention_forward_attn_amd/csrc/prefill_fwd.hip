@@ -539,7 +539,21 @@ hipError_t dispatch_d_paged(PrefillArgs a, int D, bool causal, hipStream_t strea
 
 }  // namespace
 
-hipError_t launch_prefill_paged(PrefillArgs a, int D, bool causal, int dtype, hipStream_t stream) {
+hipError_t launch_prefill_paged(PrefillArgs a, int D, bool causal, int dtype, PrefillKernel kernel,
+                                hipStream_t stream) {
+    if (kernel == PrefillKernel::kAuto) {
+        // the grid is sized by the longest request: B * Hq * max_q_len (query,
+        // head) slots, 256 per ping-pong workgroup
+        int dev = 0, n_cu = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        // (D = 128 only: at D = 64 the paged ping-pong instantiations lose the
+        // MFMA phase's operand read-ahead to the compiler's scheduling)
+        const long long rows = (long long)a.B * a.Hq * a.q_len;
+        kernel = D == 128 && rows >= 256LL * n_cu ? PrefillKernel::kPingPong : PrefillKernel::kFourWave;
+    }
+    if (kernel == PrefillKernel::kPingPong) return launch_prefill_pp_paged(a, D, causal, dtype, stream);
     if (dtype == kDtypeBF16) return dispatch_d_paged<bf16_tag>(a, D, causal, stream);
     return dispatch_d_paged<f16_tag>(a, D, causal, stream);
 }

@@ -94,7 +94,21 @@ __device__ __forceinline__ int swz(int r) {
     return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
 }
 
-template <class TAG, int D, bool CAUSAL, int NH>
+// 4 bytes per lane from global memory into LDS (lane i -> lds_base + 4 i).
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
+    __asm__ __volatile__("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+                         :
+                         : "v"(gptr), "s"(lds_base)
+                         : "m0");
+}
+
+// PAGED: a batch of ragged requests over a paged K/V cache (the FlashInfer-style
+// prefill page's `run`: query tokens of request b at qo_indptr[b] .., its key
+// pages kv_indices[kv_indptr[b] ..]), q / o token-major [total_q, Hq, D], lse
+// [total_q, Hq].  The page id of every key row of a tile is brought into a
+// per-wave LDS ring by a direct load two tiles before the tile itself, so the
+// tile loads read their page ids from LDS.
+template <class TAG, int D, bool CAUSAL, int NH, bool PAGED>
 __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
     constexpr int NW = 8;                  // waves per workgroup
     constexpr int BN = 64;                 // keys per tile
@@ -113,6 +127,8 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
 
     __shared__ __attribute__((aligned(1024))) char smem_raw[NST * STAGEB];
     lds_char* smem = (lds_char*)smem_raw;
+    // PAGED: page ids of the rows of tiles t .. t + 3, ring slot t % NST, per wave
+    __shared__ __attribute__((aligned(16))) int pg_ring[PAGED ? NW * NST * BN : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -142,11 +158,27 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
     const int pos0 = wg_pos0 + (wave % WPH) * 32;
     const int my_q = pos0 + l32;
 
-    int wg_kv_end = a.kv_len, wave_full_end = a.kv_len;
+    // ---- the request: query rows, keys, causal offset ------------------------
+    int q_len = a.q_len, kv_len = a.kv_len, delta = a.delta;
+    size_t q_tok0 = 0;  // PAGED: first query token of the request
+    int kv_page0 = 0;   // PAGED: first entry of its page list
+    if constexpr (PAGED) {
+        q_tok0 = (size_t)a.qo_indptr[b];
+        q_len = a.qo_indptr[b + 1] - (int)q_tok0;
+        kv_page0 = a.kv_indptr[b];
+        const int n_pages = a.kv_indptr[b + 1] - kv_page0;
+        kv_len = n_pages > 0 ? ((n_pages - 1) << a.page_shift) +
+                                   (a.kv_last_page_len ? a.kv_last_page_len[b] : (1 << a.page_shift))
+                             : 0;
+        delta = kv_len - q_len;
+        if (wg_pos0 >= q_len) return;  // workgroup-uniform, before any barrier: past the request's queries
+    }
+
+    int wg_kv_end = kv_len, wave_full_end = kv_len;
     if (CAUSAL) {
-        const int wg_last = min(wg_pos0 + POS, a.q_len) - 1;
-        wg_kv_end = max(0, min(a.kv_len, wg_last + a.delta + 1));
-        wave_full_end = max(0, min(a.kv_len, pos0 + a.delta + 1));
+        const int wg_last = min(wg_pos0 + POS, q_len) - 1;
+        wg_kv_end = max(0, min(kv_len, wg_last + delta + 1));
+        wave_full_end = max(0, min(kv_len, pos0 + delta + 1));
     }
     // this workgroup's key tiles t_lo .. t_lo + n_tiles - 1 (all of them unless
     // the keys are split); loop indices below are relative to t_lo
@@ -156,25 +188,37 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
     const int t_lo = min(n_all, split * per_split);
     const int n_tiles = min(n_all, t_lo + per_split) - t_lo;
     const int n_full = min(wave_full_end / BN, n_all) - t_lo;  // relative tiles below it need no mask
-    const int lim = CAUSAL ? min(my_q + a.delta + 1, a.kv_len) : a.kv_len;  // keys < lim are visible
+    const int lim = CAUSAL ? min(my_q + delta + 1, kv_len) : kv_len;  // keys < lim are visible
+
+    // element offset of query row `row` of head h in q / o, and its LSE index
+    const size_t q_head = ((size_t)b * a.Hq + h) * (size_t)q_len;
+    auto row_elt = [&](int row) -> size_t {
+        if constexpr (PAGED) return ((q_tok0 + row) * a.Hq + h) * (size_t)D;
+        return (q_head + row) * (size_t)D;
+    };
+    auto lse_idx = [&](int row) -> size_t {
+        if constexpr (PAGED) return (q_tok0 + row) * a.Hq + h;
+        return q_head + row;
+    };
+    const size_t o_row_bytes = PAGED ? (size_t)a.Hq * ROWB : (size_t)ROWB;
 
     // ---- Q (B operand of S^T = K Q^T) ---------------------------------------
-    const size_t q_head = ((size_t)b * a.Hq + h) * (size_t)a.q_len;
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + q_head * D;
     vec8 qf[DS];
     {
-        const int row = min(my_q, a.q_len - 1);
+        const uint16_t* qp = static_cast<const uint16_t*>(a.q) + row_elt(min(my_q, q_len - 1));
 #pragma unroll
-        for (int ds = 0; ds < DS; ++ds)
-            qf[ds] = __builtin_bit_cast(vec8, ld_global_16(qp + (size_t)row * D + ds * 16 + half * 8));
+        for (int ds = 0; ds < DS; ++ds) qf[ds] = __builtin_bit_cast(vec8, ld_global_16(qp + ds * 16 + half * 8));
     }
     wait_vmcnt<0>();
 
     // ---- direct global -> LDS tile loads --------------------------------------
-    const size_t kv_head = ((size_t)b * a.Hkv + g) * (size_t)a.kv_len;
+    // dense: the (b, g) plane; PAGED: head g inside the pool's token rows
+    const size_t kv_head = PAGED ? (size_t)g : ((size_t)b * a.Hkv + g) * (size_t)kv_len;
     const char* kg = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.k) + kv_head * D);
     const char* vg = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.v) + kv_head * D);
-    const int last_key = a.kv_len - 1;
+    const int last_key = kv_len - 1;
+    const int page_mask = PAGED ? (1 << a.page_shift) - 1 : 0;
+    const size_t tok_bytes = PAGED ? (size_t)a.Hkv * ROWB : (size_t)ROWB;  // bytes between key rows
     int ld_row[LPW], ld_col[LPW];
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
@@ -183,12 +227,29 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
         ld_row[j] = row;
         ld_col[j] = (pc ^ swz<D>(row)) * 16;
     }
+    // PAGED: this wave's page-id ring; lane i of the load for tile t fetches the
+    // page of key row i
+    const int* pg_wave = pg_ring + (PAGED ? wave * NST * BN : 0);
+    auto issue_pages = [&](int t) {
+        if constexpr (PAGED) {
+            const int key = min((t_lo + t) * BN + lane, last_key);
+            const int* src = a.kv_indices + kv_page0 + (key >> a.page_shift);
+            dma4(src, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(pg_wave + (t % NST) * BN)));
+        }
+    };
     auto issue_tile = [&](int t) {
         const int t0 = (t_lo + t) * BN;
         lds_char* st = smem + (t % NST) * STAGEB;
 #pragma unroll
         for (int j = 0; j < LPW; ++j) {
-            const size_t off = (size_t)min(t0 + ld_row[j], last_key) * ROWB + ld_col[j];
+            const int key = min(t0 + ld_row[j], last_key);
+            size_t off;
+            if constexpr (PAGED) {
+                const int page = pg_wave[(t % NST) * BN + ld_row[j]];
+                off = (((size_t)page << a.page_shift) + (size_t)(key & page_mask)) * tok_bytes + ld_col[j];
+            } else {
+                off = (size_t)key * ROWB + ld_col[j];
+            }
             const uint32_t dst = (uint32_t)(uintptr_t)(st + (wave * LPW + j) * 1024);
             dma16(kg + off, __builtin_amdgcn_readfirstlane(dst));
             dma16(vg + off, __builtin_amdgcn_readfirstlane(dst + TILEB));
@@ -362,19 +423,35 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
     // tile t+1: scores of t+1 and P.V of t) for each t, the last P.V alone.
     // Tile t must be in LDS (this wave's loads done, then the barrier) from
     // phase 2t on; tile t+2 is issued right after the barrier of phase 2t.
+    // PAGED: the page ids of tile t + 4 are loaded right after tile t + 2, so at
+    // phase 2t the loads younger than those of tile t + 2's pages are tile t+1's
+    // and the pages of t + 3.
     if (n_tiles > 0) {
+        if constexpr (PAGED) {
+            issue_pages(0);
+            if (n_tiles > 1) issue_pages(1);
+            wait_vmcnt<0>();
+            __asm__ __volatile__("" ::: "memory");  // the page ids are read below
+        }
         issue_tile(0);
+        if (n_tiles > 2) issue_pages(2);
         if (n_tiles > 1) issue_tile(1);
+        if (n_tiles > 3) issue_pages(3);
         int p = 0;
         auto sync = [&]() {
             if ((p & 1) == 0) {
                 const int t = p >> 1;
                 if (t < n_tiles) {
-                    if (t + 1 < n_tiles) wait_vmcnt<2 * LPW>(); else wait_vmcnt<0>();
+                    if (PAGED && t + 3 < n_tiles) wait_vmcnt<2 * LPW + 1>();   // tile t, pages of t + 2
+                    else if (t + 1 < n_tiles) wait_vmcnt<2 * LPW>();           // tile t (pages of t + 2 if any)
+                    else wait_vmcnt<0>();
                 }
             }
             barrier_no_fence();
-            if ((p & 1) == 0 && (p >> 1) + 2 < n_tiles) issue_tile((p >> 1) + 2);
+            if ((p & 1) == 0 && (p >> 1) + 2 < n_tiles) {
+                issue_tile((p >> 1) + 2);
+                if ((p >> 1) + 4 < n_tiles) issue_pages((p >> 1) + 4);
+            }
             ++p;
         };
         if (grp) sync();  // group 1 starts one phase later
@@ -394,7 +471,8 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
     }
 
     // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----------------------------
-    // The wave's 32 rows are consecutive in o.  They are staged in LDS and
+    // The wave's 32 rows are consecutive in o (PAGED: one row of head h every
+    // Hq rows).  They are staged in LDS and
     // written as whole rows (a store instruction covers 64 / CPR full rows).
     // Staging area: wave w uses 32 rows of stage (n_tiles + w / 4) % NST, which
     // no wave reads any more (the last tile, still read by group 1's final
@@ -402,10 +480,10 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
     // the last are never issued).  Each wave reads back only what it wrote.
     const float l_tot = l + xor32(l);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (a.kv_splits > 1) {
+    if (!PAGED && a.kv_splits > 1) {
         // partial result of this key range: O_s = acc / l (0 when none of its
         // keys is visible to the row) and LSE_s (-inf then), both fp32
-        if (my_q < a.q_len) {
+        if (my_q < q_len) {
             const size_t prow = (q_head + my_q) * a.kv_splits + split;
             float* po = a.part_o + prow * D;
 #pragma unroll
@@ -433,17 +511,17 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
                 chunk[j];
         }
         constexpr int RPI = 64 / CPR;  // rows per store instruction
-        char* og = reinterpret_cast<char*>(static_cast<uint16_t*>(a.o) + (q_head + pos0) * D);
+        char* og = reinterpret_cast<char*>(static_cast<uint16_t*>(a.o) + row_elt(pos0));
         const int cc = lane % CPR;
 #pragma unroll
         for (int k = 0; k < 32 / RPI; ++k) {
             const int rr = RPI * k + lane / CPR;
             const u32x4 v =
                 *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(ob + rr * ROWB + ((cc ^ oswz(rr)) << 4));
-            if (pos0 + rr < a.q_len) *reinterpret_cast<u32x4*>(og + rr * ROWB + cc * 16) = v;
+            if (pos0 + rr < q_len) *reinterpret_cast<u32x4*>(og + rr * o_row_bytes + cc * 16) = v;
         }
     }
-    if (my_q < a.q_len && half == 0) a.lse[q_head + my_q] = l_tot > 0.f ? (m + fast_log2(l_tot)) * kLn2 : -INFINITY;
+    if (my_q < q_len && half == 0) a.lse[lse_idx(my_q)] = l_tot > 0.f ? (m + fast_log2(l_tot)) * kLn2 : -INFINITY;
 }
 
 // Merge of the key ranges of a split-KV prefill, the LSE merge of the split-K
@@ -486,14 +564,14 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a, long 
     if (d0 == 0) a.lse[row] = W > 0.f ? M + fast_log2(W) * kLn2 : -INFINITY;
 }
 
-template <class TAG, int D, bool CAUSAL, int NH>
+template <class TAG, int D, bool CAUSAL, int NH, bool PAGED>
 hipError_t launch_pp(PrefillArgs a, hipStream_t stream) {
     constexpr int POS = 256 / NH;
     a.n_pos_tiles = (a.q_len + POS - 1) / POS;
     a.n_rest = a.B * a.Hkv * (a.group / NH);
     const long long blocks = (long long)a.n_pos_tiles * a.n_rest * (a.kv_splits > 1 ? a.kv_splits : 1);
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((prefill_fwd_pp<TAG, D, CAUSAL, NH>), dim3((unsigned)blocks), dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((prefill_fwd_pp<TAG, D, CAUSAL, NH, PAGED>), dim3((unsigned)blocks), dim3(512), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.kv_splits <= 1) return e;
     const long long rows = (long long)a.B * a.Hq * a.q_len;
@@ -503,18 +581,19 @@ hipError_t launch_pp(PrefillArgs a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <class TAG, int D, bool CAUSAL>
+template <class TAG, int D, bool CAUSAL, bool PAGED>
 hipError_t dispatch_nh(PrefillArgs a, hipStream_t stream) {
-    if (a.group % 8 == 0) return launch_pp<TAG, D, CAUSAL, 8>(a, stream);
-    if (a.group % 4 == 0) return launch_pp<TAG, D, CAUSAL, 4>(a, stream);
-    if (a.group % 2 == 0) return launch_pp<TAG, D, CAUSAL, 2>(a, stream);
-    return launch_pp<TAG, D, CAUSAL, 1>(a, stream);
+    if (a.group % 8 == 0) return launch_pp<TAG, D, CAUSAL, 8, PAGED>(a, stream);
+    if (a.group % 4 == 0) return launch_pp<TAG, D, CAUSAL, 4, PAGED>(a, stream);
+    if (a.group % 2 == 0) return launch_pp<TAG, D, CAUSAL, 2, PAGED>(a, stream);
+    return launch_pp<TAG, D, CAUSAL, 1, PAGED>(a, stream);
 }
 
-template <class TAG>
+template <class TAG, bool PAGED>
 hipError_t dispatch_d(PrefillArgs a, int D, bool causal, hipStream_t stream) {
-    if (D == 64) return causal ? dispatch_nh<TAG, 64, true>(a, stream) : dispatch_nh<TAG, 64, false>(a, stream);
-    return causal ? dispatch_nh<TAG, 128, true>(a, stream) : dispatch_nh<TAG, 128, false>(a, stream);
+    if (D == 64)
+        return causal ? dispatch_nh<TAG, 64, true, PAGED>(a, stream) : dispatch_nh<TAG, 64, false, PAGED>(a, stream);
+    return causal ? dispatch_nh<TAG, 128, true, PAGED>(a, stream) : dispatch_nh<TAG, 128, false, PAGED>(a, stream);
 }
 
 }  // namespace
@@ -531,8 +610,14 @@ hipError_t launch_prefill_split(PrefillArgs a, int D, bool causal, int dtype, hi
 }
 
 hipError_t launch_prefill_pp(PrefillArgs a, int D, bool causal, int dtype, hipStream_t stream) {
-    if (dtype == kDtypeBF16) return dispatch_d<bf16_tag>(a, D, causal, stream);
-    return dispatch_d<f16_tag>(a, D, causal, stream);
+    if (dtype == kDtypeBF16) return dispatch_d<bf16_tag, false>(a, D, causal, stream);
+    return dispatch_d<f16_tag, false>(a, D, causal, stream);
+}
+
+hipError_t launch_prefill_pp_paged(PrefillArgs a, int D, bool causal, int dtype, hipStream_t stream) {
+    a.kv_splits = 1;
+    if (dtype == kDtypeBF16) return dispatch_d<bf16_tag, true>(a, D, causal, stream);
+    return dispatch_d<f16_tag, true>(a, D, causal, stream);
 }
 
 }  // namespace gqa

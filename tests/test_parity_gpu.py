@@ -443,10 +443,13 @@ PAGED_PREFILL = [
 ]
 
 
+# both kernels have a paged mode (chosen by the grid size; forced here)
+@pytest.mark.parametrize("kernel", PREFILL_KERNELS)
 @pytest.mark.parametrize("case", PAGED_PREFILL, ids=lambda c: "-".join(map(str, c[:6])))
-def test_prefill_paged_cases(case):
+def test_prefill_paged_cases(case, kernel, monkeypatch):
+    monkeypatch.setenv("GQA_ATTN_PREFILL_KERNEL", kernel)
     Hq, Hkv, D, dt, ps, causal, lens = case
-    print(f"paged prefill case {case[:6]}", flush=True)
+    print(f"paged prefill case {case[:6]} kernel {kernel}", flush=True)
     if isinstance(lens[0], list):
         inp = W.make_paged_prefill(len(lens[0]), Hq, Hkv, D, dt, seed=Hq + D + ps, page_size=ps,
                                    q_lens=lens[0], kv_lens=lens[1])
@@ -460,8 +463,10 @@ def test_prefill_paged_cases(case):
     check(o, l, o_ref, l_ref, dt, str(case[:6]))
 
 
-def test_prefill_paged_full_pages_without_last_len():
+@pytest.mark.parametrize("kernel", PREFILL_KERNELS)
+def test_prefill_paged_full_pages_without_last_len(kernel, monkeypatch):
     # kv_last_page_len omitted: every page is full
+    monkeypatch.setenv("GQA_ATTN_PREFILL_KERNEL", kernel)
     inp = W.make_paged_prefill(3, 8, 2, 64, "bf16", seed=50, page_size=32, q_lens=[40, 64, 3],
                                kv_lens=[64, 96, 32])
     o, l = gpu_prefill_paged(inp, True, 0.125, last=False)
@@ -469,15 +474,17 @@ def test_prefill_paged_full_pages_without_last_len():
     check(o, l, o_ref, l_ref, "bf16", "full pages")
 
 
-def test_prefill_paged_equals_dense_forward(monkeypatch):
-    # one request over an identity page table is the dense forward of the same K/V
+@pytest.mark.parametrize("kernel", PREFILL_KERNELS)
+def test_prefill_paged_equals_dense_forward(kernel, monkeypatch):
+    # one request over an identity page table is the dense forward of the same
+    # K/V on the same kernel
+    monkeypatch.setenv("GQA_ATTN_PREFILL_KERNEL", kernel)
     inp = W.make_paged_prefill(1, 8, 2, 128, "bf16", seed=51, page_size=64, q_lens=[300], kv_lens=[700],
                                permute=False)
     o1, l1 = gpu_prefill_paged(inp, True, 0.088)
     kd = inp.k_cache.reshape(-1, 2, 128)[:700].permute(1, 0, 2).unsqueeze(0).contiguous()
     vd = inp.v_cache.reshape(-1, 2, 128)[:700].permute(1, 0, 2).unsqueeze(0).contiguous()
     qd = inp.q.permute(1, 0, 2).unsqueeze(0).contiguous()
-    monkeypatch.setenv("GQA_ATTN_PREFILL_KERNEL", "fourwave")  # the kernel the paged path uses
     o2, l2 = gpu_fwd(qd, kd, vd, True, 0.088)
     o2 = o2.double().cpu().numpy()[0].transpose(1, 0, 2)
     l2 = l2.double().cpu().numpy()[0].T
@@ -485,7 +492,9 @@ def test_prefill_paged_equals_dense_forward(monkeypatch):
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
-def test_prefill_paged_workload_sampled():
+@pytest.mark.parametrize("kernel", PREFILL_KERNELS)
+def test_prefill_paged_workload_sampled(kernel, monkeypatch):
+    monkeypatch.setenv("GQA_ATTN_PREFILL_KERNEL", kernel)
     spec = W.RAGGED_PAGED_PREFILL
     print("workload ragged_paged_prefill", flush=True)
     inp = W.make_paged_prefill_spec(spec)
