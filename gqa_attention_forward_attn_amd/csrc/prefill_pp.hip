@@ -145,18 +145,48 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
         split = id % a.kv_splits;
         id /= a.kv_splits;
     }
-    int pt = id / a.n_rest;
-    int rest = id - pt * a.n_rest;
-    if (CAUSAL) pt = a.n_pos_tiles - 1 - pt;  // longest rows first
     const int hgroups = a.group / NH;
-    const int hg = rest % hgroups;
-    rest /= hgroups;
-    const int g = rest % a.Hkv;
-    const int b = rest / a.Hkv;
+    int pt, hg, g, b;
+    bool from_end = false;  // PAGED: position tile counted from the request's last query
+    if (PAGED && a.B <= 64) {
+        // Ragged batch: workgroups in order of (i, request), i = position tile
+        // counted from each request's end (its rows see the most keys), over the
+        // requests that have an i-th tile; the heads fastest.  Workgroups past
+        // the last such item (the grid is sized by the longest request) come
+        // last and exit, so that they do not hold up the dispatch of real work.
+        const int n_hk = a.Hkv * hgroups;
+        int item = id / n_hk;
+        int hk = id - item * n_hk;
+        hg = hk % hgroups;
+        g = hk / hgroups;
+        const int nq = lane < a.B ? a.qo_indptr[lane + 1] - a.qo_indptr[lane] : 0;
+        const int npt = (nq + POS - 1) / POS;
+        b = -1;
+        pt = 0;
+        for (int i = 0; i < a.n_pos_tiles; ++i) {
+            const uint64_t has = __builtin_amdgcn_ballot_w64(npt > i);
+            const int c = __builtin_popcountll(has);
+            if (item < c) {
+                // the item-th request (in index order) that has an i-th tile
+                const int rank = __builtin_popcountll(has & ((1ull << lane) - 1ull));
+                b = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(npt > i && rank == item));
+                pt = i;
+                break;
+            }
+            item -= c;
+        }
+        if (b < 0) return;  // workgroup-uniform, before any barrier: no item left
+        from_end = true;
+    } else {
+        pt = id / a.n_rest;
+        int rest = id - pt * a.n_rest;
+        if (CAUSAL) pt = a.n_pos_tiles - 1 - pt;  // longest rows first
+        hg = rest % hgroups;
+        rest /= hgroups;
+        g = rest % a.Hkv;
+        b = rest / a.Hkv;
+    }
     const int h = g * a.group + hg * NH + wave / WPH;
-    const int wg_pos0 = pt * POS;
-    const int pos0 = wg_pos0 + (wave % WPH) * 32;
-    const int my_q = pos0 + l32;
 
     // ---- the request: query rows, keys, causal offset ------------------------
     int q_len = a.q_len, kv_len = a.kv_len, delta = a.delta;
@@ -171,8 +201,14 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
                                    (a.kv_last_page_len ? a.kv_last_page_len[b] : (1 << a.page_shift))
                              : 0;
         delta = kv_len - q_len;
-        if (wg_pos0 >= q_len) return;  // workgroup-uniform, before any barrier: past the request's queries
     }
+    // first query position of the workgroup (bottom-aligned tiles may start
+    // before the request's first query: those rows are not computed or stored)
+    const int wg_pos0 = from_end ? q_len - (pt + 1) * POS : pt * POS;
+    if (PAGED && wg_pos0 >= q_len) return;  // workgroup-uniform, before any barrier: past the request's queries
+    const int pos0 = wg_pos0 + (wave % WPH) * 32;
+    const int my_q = pos0 + l32;
+    const bool row_ok = my_q >= 0 && my_q < q_len;
 
     int wg_kv_end = kv_len, wave_full_end = kv_len;
     if (CAUSAL) {
@@ -205,7 +241,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
     // ---- Q (B operand of S^T = K Q^T) ---------------------------------------
     vec8 qf[DS];
     {
-        const uint16_t* qp = static_cast<const uint16_t*>(a.q) + row_elt(min(my_q, q_len - 1));
+        const uint16_t* qp = static_cast<const uint16_t*>(a.q) + row_elt(min(max(my_q, 0), q_len - 1));
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds) qf[ds] = __builtin_bit_cast(vec8, ld_global_16(qp + ds * 16 + half * 8));
     }
@@ -511,17 +547,19 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
                 chunk[j];
         }
         constexpr int RPI = 64 / CPR;  // rows per store instruction
-        char* og = reinterpret_cast<char*>(static_cast<uint16_t*>(a.o) + row_elt(pos0));
+        char* og0 = reinterpret_cast<char*>(static_cast<uint16_t*>(a.o) + row_elt(0));  // the head's row 0
         const int cc = lane % CPR;
 #pragma unroll
         for (int k = 0; k < 32 / RPI; ++k) {
             const int rr = RPI * k + lane / CPR;
             const u32x4 v =
                 *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(ob + rr * ROWB + ((cc ^ oswz(rr)) << 4));
-            if (pos0 + rr < q_len) *reinterpret_cast<u32x4*>(og + rr * o_row_bytes + cc * 16) = v;
+            const int row = pos0 + rr;
+            if (row >= 0 && row < q_len)
+                *reinterpret_cast<u32x4*>(og0 + (size_t)row * o_row_bytes + cc * 16) = v;
         }
     }
-    if (my_q < q_len && half == 0) a.lse[lse_idx(my_q)] = l_tot > 0.f ? (m + fast_log2(l_tot)) * kLn2 : -INFINITY;
+    if (row_ok && half == 0) a.lse[lse_idx(my_q)] = l_tot > 0.f ? (m + fast_log2(l_tot)) * kLn2 : -INFINITY;
 }
 
 // Merge of the key ranges of a split-KV prefill, the LSE merge of the split-K
