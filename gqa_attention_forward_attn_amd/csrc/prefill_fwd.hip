@@ -68,18 +68,45 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_mfma(PrefillArgs a) {
     const int l32 = lane & 31;
 
     // ---- work item: (position tile, batch, K/V head, head group) ----------
-    int pt = blockIdx.x / a.n_rest;
-    int rest = blockIdx.x - pt * a.n_rest;
-    if (CAUSAL) pt = a.n_pos_tiles - 1 - pt;  // longest rows first
     const int hgroups = a.group / NH;
-    const int hg = rest % hgroups;
-    rest /= hgroups;
-    const int g = rest % a.Hkv;
-    const int b = rest / a.Hkv;
+    int pt, hg, g, b;
+    bool from_end = false;  // PAGED: position tile counted from the request's last query
+    if (PAGED && a.B <= 64) {
+        // Ragged batch: only real items, in the order (i, request) with i the
+        // position tile counted from the request's end, heads fastest; the
+        // grid's surplus workgroups come last (as in prefill_pp.hip).
+        const int n_hk = a.Hkv * hgroups;
+        int item = blockIdx.x / n_hk;
+        const int hk = blockIdx.x - item * n_hk;
+        hg = hk % hgroups;
+        g = hk / hgroups;
+        const int nq = lane < a.B ? a.qo_indptr[lane + 1] - a.qo_indptr[lane] : 0;
+        const int npt = (nq + POS - 1) / POS;
+        b = -1;
+        pt = 0;
+        for (int i = 0; i < a.n_pos_tiles; ++i) {
+            const uint64_t has = __builtin_amdgcn_ballot_w64(npt > i);
+            const int c = __builtin_popcountll(has);
+            if (item < c) {
+                const int rank = __builtin_popcountll(has & ((1ull << lane) - 1ull));
+                b = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(npt > i && rank == item));
+                pt = i;
+                break;
+            }
+            item -= c;
+        }
+        if (b < 0) return;  // workgroup-uniform, before any barrier: no item left
+        from_end = true;
+    } else {
+        pt = blockIdx.x / a.n_rest;
+        int rest = blockIdx.x - pt * a.n_rest;
+        if (CAUSAL) pt = a.n_pos_tiles - 1 - pt;  // longest rows first
+        hg = rest % hgroups;
+        rest /= hgroups;
+        g = rest % a.Hkv;
+        b = rest / a.Hkv;
+    }
     const int h = g * a.group + hg * NH + wave / WPH;
-    const int wg_pos0 = pt * POS;
-    const int pos0 = wg_pos0 + (wave % WPH) * 32;
-    const int my_q = pos0 + l32;
 
     // ---- the request: query rows, keys, causal offset ------------------------
     int q_len = a.q_len, kv_len = a.kv_len, delta = a.delta;
@@ -94,8 +121,13 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_mfma(PrefillArgs a) {
                                    (a.kv_last_page_len ? a.kv_last_page_len[b] : (1 << a.page_shift))
                              : 0;
         delta = kv_len - q_len;
-        if (wg_pos0 >= q_len) return;  // workgroup-uniform: past this request's queries
     }
+    // first query position of the workgroup (bottom-aligned tiles may start
+    // before the request's first query: those rows are not computed or stored)
+    const int wg_pos0 = from_end ? q_len - (pt + 1) * POS : pt * POS;
+    if (PAGED && wg_pos0 >= q_len) return;  // workgroup-uniform: past this request's queries
+    const int pos0 = wg_pos0 + (wave % WPH) * 32;
+    const int my_q = pos0 + l32;
     // element offset of query row `row` of head h (q and o), and its LSE index
     auto q_off = [&](int row) -> size_t {
         if constexpr (PAGED) return ((q_tok0 + row) * a.Hq + h) * (size_t)D;
@@ -114,16 +146,16 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_mfma(PrefillArgs a) {
         const int wg_last = min(wg_pos0 + POS, q_len) - 1;
         wg_kv_end = max(0, min(kv_len, wg_last + delta + 1));
         const int w_last = min(pos0 + 32, q_len) - 1;
-        wave_kv_end = pos0 < q_len ? max(0, min(kv_len, w_last + delta + 1)) : 0;
+        wave_kv_end = pos0 < q_len && pos0 + 32 > 0 ? max(0, min(kv_len, w_last + delta + 1)) : 0;
         wave_full_end = max(0, min(kv_len, pos0 + delta + 1));
-    } else if (pos0 >= q_len) {
+    } else if (pos0 >= q_len || pos0 + 32 <= 0) {
         wave_kv_end = 0;
     }
     const int n_tiles = (wg_kv_end + BN - 1) / BN;
 
     // ---- Q: B operand of S^T = K Q^T, resident in registers ---------------
     const uint16_t* qp = static_cast<const uint16_t*>(a.q);
-    const int q_row = min(my_q, q_len - 1);
+    const int q_row = min(max(my_q, 0), q_len - 1);
     vec8 qf[DS];
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds)
@@ -315,9 +347,9 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_mfma(PrefillArgs a) {
 
     // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2 -------------------
     const float l_tot = l + xor32(l);
-    const bool valid = my_q < q_len;
+    const bool valid = my_q >= 0 && my_q < q_len;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    store_acc_row(TAG(), acc, inv, static_cast<uint16_t*>(a.o) + q_off(min(my_q, q_len - 1)), half, valid);
+    store_acc_row(TAG(), acc, inv, static_cast<uint16_t*>(a.o) + q_off(min(max(my_q, 0), q_len - 1)), half, valid);
     if (valid && half == 0) a.lse[lse_off(my_q)] = l_tot > 0.f ? (m + fast_log2(l_tot)) * kLn2 : -INFINITY;
 }
 
