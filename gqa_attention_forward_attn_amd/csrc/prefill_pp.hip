@@ -556,7 +556,9 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
                 *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(ob + rr * ROWB + ((cc ^ oswz(rr)) << 4));
             const int row = pos0 + rr;
             if (row >= 0 && row < q_len)
-                *reinterpret_cast<u32x4*>(og0 + (size_t)row * o_row_bytes + cc * 16) = v;
+                // whole 128-byte lines: streamed past L2 (non-temporal), so the
+                // output does not evict K/V tiles other workgroups still read
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(og0 + (size_t)row * o_row_bytes + cc * 16));
         }
     }
     if (row_ok && half == 0) a.lse[lse_idx(my_q)] = l_tot > 0.f ? (m + fast_log2(l_tot)) * kLn2 : -INFINITY;
