@@ -730,91 +730,65 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel_fp8(DecodeArgs
     }
 }
 
-// One workgroup per query row (b, h, i): merge the non-empty chunks' partial
-// results.  Wave w merges the chunks s = w (mod 4) with weights relative to its
-// own maximum LSE (independent loads, eight at a time), and the four waves are
-// merged through LDS.  Chunks with LSE = -inf (no visible key) weigh 0.
+// Merge of the non-empty chunks' partial results of each query row (b, h, i),
+// one wave per row (four rows per workgroup).  The LSEs and partial outputs of
+// up to 16 chunks are loaded together, so a row costs one memory round trip
+// per 16 chunks; the merge keeps a running maximum across those steps.  Chunks
+// with LSE = -inf (no visible key) weigh 0.
 template <class TAG, int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     constexpr int PER = D / 64;  // output dims per lane
-    constexpr int CW = 4;        // waves
-    __shared__ float s_m[CW], s_w[CW], s_o[CW][D];
+    constexpr int CH = 16;       // chunks per step
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int row = blockIdx.x;  // (b * Hq + h) * q_len + i
-    const int len = a.seq_lens[row / (a.Hq * a.q_len)];
+    const long long rows = (long long)a.B * a.Hq * a.q_len;
+    const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b * Hq + h) * q_len + i
+    if (row >= rows) return;
+    const int len = a.seq_lens[row / ((long long)a.Hq * a.q_len)];
     const int nv = len > 0 ? (len + chunk_tokens(len, a.n_splits) - 1) / chunk_tokens(len, a.n_splits) : 0;
-    const float* pl = a.part_lse + (size_t)row * a.n_splits;
-    const float* po = a.part_o + (size_t)row * a.n_splits * D + lane * PER;
+    const float* pl = a.part_lse + row * a.n_splits;
+    const float* po = a.part_o + row * a.n_splits * D + lane * PER;
 
-    // this wave's chunks: s = wave + CW * t, t < nt
-    const int nt = nv > wave ? (nv - wave + CW - 1) / CW : 0;
-    float M = -INFINITY;
-    for (int t = lane; t < nt; t += 64) M = fmaxf(M, pl[wave + CW * t]);
-#pragma unroll
-    for (int x = 32; x >= 1; x >>= 1) M = fmaxf(M, shfl_xor(M, x));
-    float W = 0.f, O[PER];
+    float M = -INFINITY, W = 0.f, O[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) O[i] = 0.f;
-    for (int t0 = 0; t0 < nt; t0 += 64) {
-        const int n = min(64, nt - t0);
-        const float lv = lane < n ? pl[wave + CW * (t0 + lane)] : -INFINITY;
+    for (int s0 = 0; s0 < nv; s0 += CH) {
+        const int n = min(CH, nv - s0);
+        const float lv = lane < n ? pl[s0 + lane] : -INFINITY;
+        float x[CH][PER];
+#pragma unroll
+        for (int u = 0; u < CH; ++u)  // chunks past n repeat the last one (their weight is 0)
+#pragma unroll
+            for (int i = 0; i < PER; ++i) x[u][i] = po[(size_t)min(s0 + u, nv - 1) * D + i];
+        float mb = lv;
+#pragma unroll
+        for (int k = 32; k >= 1; k >>= 1) mb = fmaxf(mb, shfl_xor(mb, k));
+        const float mn = fmaxf(M, mb);
+        if (mn == -INFINITY) continue;  // no non-empty chunk so far
+        const float sc = M == -INFINITY ? 0.f : fast_exp2((M - mn) * kLog2e);
+        M = mn;
+        W *= sc;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) O[i] *= sc;
         const float w = lv == -INFINITY ? 0.f : fast_exp2((lv - M) * kLog2e);
-        W += w;
-        int t = 0;
-        for (; t + 8 <= n; t += 8) {
-            float x[8][PER];
+        W += w;  // this lane's chunk (summed over the wave below)
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < CH; ++u) {
+            const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), u));
 #pragma unroll
-                for (int i = 0; i < PER; ++i) x[u][i] = po[(size_t)(wave + CW * (t0 + t + u)) * D + i];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), t + u));
-#pragma unroll
-                for (int i = 0; i < PER; ++i) O[i] = fmaf(wu, x[u][i], O[i]);
-            }
-        }
-        for (; t < n; ++t) {
-            const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), t));
-#pragma unroll
-            for (int i = 0; i < PER; ++i) O[i] = fmaf(wu, po[(size_t)(wave + CW * (t0 + t)) * D + i], O[i]);
+            for (int i = 0; i < PER; ++i) O[i] = fmaf(wu, x[u][i], O[i]);
         }
     }
 #pragma unroll
-    for (int x = 32; x >= 1; x >>= 1) W += shfl_xor(W, x);
-    if (lane == 0) {
-        s_m[wave] = M;
-        s_w[wave] = W;
-    }
-#pragma unroll
-    for (int i = 0; i < PER; ++i) s_o[wave][lane * PER + i] = O[i];
-    __syncthreads();
-    if (wave != 0) return;
-    float Mt = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < CW; ++w) Mt = fmaxf(Mt, s_m[w]);
-    float Wt = 0.f, Ot[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) Ot[i] = 0.f;
-    if (Mt != -INFINITY) {
-#pragma unroll
-        for (int w = 0; w < CW; ++w) {
-            const float e = s_m[w] == -INFINITY ? 0.f : fast_exp2((s_m[w] - Mt) * kLog2e);
-            Wt += e * s_w[w];
-#pragma unroll
-            for (int i = 0; i < PER; ++i) Ot[i] = fmaf(e, s_o[w][lane * PER + i], Ot[i]);
-        }
-    }
-    const float inv = Wt > 0.f ? 1.f / Wt : 0.f;
+    for (int k = 32; k >= 1; k >>= 1) W += shfl_xor(W, k);
+    const float inv = W > 0.f ? 1.f / W : 0.f;
     uint16_t* op = static_cast<uint16_t*>(a.o) + (size_t)row * D + lane * PER;
     if (PER == 2) {
-        *reinterpret_cast<uint32_t*>(op) = pack2(TAG(), Ot[0] * inv, Ot[PER - 1] * inv);
+        *reinterpret_cast<uint32_t*>(op) = pack2(TAG(), O[0] * inv, O[PER - 1] * inv);
     } else {
-        const uint32_t w = pack2(TAG(), Ot[0] * inv, 0.f);
+        const uint32_t w = pack2(TAG(), O[0] * inv, 0.f);
         *op = (uint16_t)(w & 0xffff);
     }
-    if (lane == 0) a.lse[row] = Wt > 0.f ? Mt + fast_log2(Wt) * kLn2 : -INFINITY;
+    if (lane == 0) a.lse[row] = W > 0.f ? M + fast_log2(W) * kLn2 : -INFINITY;
 }
 
 template <class TAG, int D, int PG>
@@ -827,8 +801,8 @@ hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long long rows = (long long)a.B * a.Hq * a.q_len;
-    if (rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((decode_combine_kernel<TAG, D>), dim3((unsigned)rows), dim3(256), 0, stream, a);
+    if ((rows + 3) / 4 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((decode_combine_kernel<TAG, D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -841,7 +815,8 @@ hipError_t launch_split_fp8(const DecodeArgs& a, hipStream_t stream) {
                        dim3(DEC8_NW * 64), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_combine_kernel<TAG, D>), dim3((unsigned)(a.B * a.Hq)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((decode_combine_kernel<TAG, D>), dim3((unsigned)(((long long)a.B * a.Hq + 3) / 4)), dim3(256), 0,
+                       stream, a);
     return hipGetLastError();
 }
 
