@@ -440,7 +440,8 @@ PAGED_PREFILL = [
     (32, 4, 128, "bf16", 64, True, (3, (1, 400), (0, 500))),      # G = 8
     (6, 3, 64, "bf16", 256, False, (4, (1, 200), (0, 300))),      # G = 2, non-causal
     (16, 2, 128, "f16", 4, True, ([200, 64, 7, 130], [150, 64, 3, 400])),  # some q_len > kv_len
-    (8, 2, 128, "bf16", 16, True, (70, (1, 40), (0, 60))),       # > 64 requests: the dense work order
+    (8, 2, 128, "bf16", 16, True, (70, (1, 40), (0, 60))),       # > 64 requests (work order over 2 lane chunks)
+    (4, 2, 64, "bf16", 16, True, (520, (1, 8), (0, 12))),        # > 512 requests: the dense work order
 ]
 
 
