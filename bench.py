@@ -44,9 +44,9 @@ METRIC = "attention fwd TFLOP/s + % bf16 MFMA peak; decode GB/s + % HBM peak"
 # other source reports traffic null.
 TRAFFIC_MEASUREMENT = {
     "source": "gqa_attention_forward_attn_amd/csrc/prefill_pp.hip",
-    "sha1": "3fa35f48733457010df41975b5f31a18f99615f0",
-    "fetch_kib": 24762.4, "write_kib": 33280.0,
-    "copy_fetch_kib": 262156.4, "copy_write_kib": 524288.0,
+    "sha1": "63b14774f51d3b92a42b64f075be1d0e2669d24f",
+    "fetch_kib": 25018.6, "write_kib": 33280.0,
+    "copy_fetch_kib": 262156.0, "copy_write_kib": 524288.0,
 }
 
 
