@@ -178,7 +178,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
     constexpr int PER_SLICE = 2 * NI;
     static_assert((NST - 1) * PER_SLICE < 64, "vmcnt range");
     static_assert((NST & (NST - 1)) == 0, "NST must be a power of two");
-    static_assert(NW * 16 * (D + 2) * 4 <= NW * WAVEB, "merge buffers must fit in the ring");
+    static_assert(NW * 16 * (D + 3) * 4 <= NW * WAVEB, "merge buffers must fit in the ring");
 
     __shared__ __attribute__((aligned(1024))) char smem_raw[NW * WAVEB];
     lds_char* smem = (lds_char*)smem_raw;
@@ -382,24 +382,34 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
     }
     __syncthreads();
     const size_t prow = qrow0 * a.n_splits + s;  // partial row of the block's first column
-    for (int i = tid; i < nh * D; i += NW * 64) {
-        const int h = i / D, d = i % D;
+    // per column: the waves' weights relative to the largest running max,
+    // divided by the column's sum, and its LSE; a column with no visible key
+    // in this chunk (a query before the chunk's keys) gives (0, -inf)
+    float* se = sl + NW * 16;  // [NW][16]
+    if (tid < nh) {
+        const int h = tid;
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < NW; ++w) M = fmaxf(M, sm[w * 16 + h]);
-        float L = 0.f, O = 0.f;
+        float e[NW], L = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
             const float mw = sm[w * 16 + h];
-            const float e = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
-            L += e * sl[w * 16 + h];
-            O += e * sacc[(w * 16 + h) * D + d];
+            e[w] = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
+            L += e[w] * sl[w * 16 + h];
         }
-        // a column with no visible key in this chunk (a query before the chunk's
-        // keys) gives (0, -inf)
-        const size_t row = prow + (size_t)h * a.n_splits;
-        a.part_o[row * D + d] = L > 0.f ? O / L : 0.f;
-        if (d == 0) a.part_lse[row] = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) se[w * 16 + h] = e[w] * inv;
+        a.part_lse[prow + (size_t)h * a.n_splits] = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
+    }
+    __syncthreads();
+    for (int i = tid; i < nh * D; i += NW * 64) {
+        const int h = i / D, d = i % D;
+        float O = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) O = fmaf(se[w * 16 + h], sacc[(w * 16 + h) * D + d], O);
+        a.part_o[(prow + (size_t)h * a.n_splits) * D + d] = O;
     }
 }
 
