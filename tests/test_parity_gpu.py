@@ -620,3 +620,158 @@ def test_decode_fp8_dense_matches_paged_and_page_order():
                           a.page_size, a.max_kv_len)
     o3, l3 = gpu_decode_fp8(b, 4, 0.125)
     assert np.array_equal(o1, o3) and np.array_equal(l1, l3)
+
+
+# ---- operands past 2^31 elements: every offset is 64-bit ---------------------------
+# Each case puts the data it checks where element offsets are >= 2^31 (byte
+# offsets >= 4 GiB) and fills everything else with NaN: an offset that wrapped
+# at 32 bits would read NaN (or write the wrong rows) and fail the comparison.
+# The GPU result must also equal, bit for bit, the same call on a compact copy.
+
+BIG = 2 ** 31
+NAN_E4M3 = 0x7F                 # E4M3 byte with every exponent and mantissa bit set: NaN
+NAN_SCALE_SHIFT = 0x7E007E00    # fp16 NaN in both halves of a scale-shift word
+
+
+def _release():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _pool(small, first, fill):
+    """`small` (pages on the host) at page ids first.. of a pool on the GPU whose
+    other pages hold `fill`."""
+    pool = torch.full((first + small.shape[0],) + tuple(small.shape[1:]), fill, dtype=small.dtype, device="cuda")
+    pool[first:] = small.cuda()
+    return pool
+
+
+def _shift_table(t, first):
+    return torch.where(t >= 0, t + first, t)
+
+
+def _last_batch(shape, data):
+    """A NaN tensor of `shape` on the GPU whose last batch entry is `data` [1, ...]."""
+    x = torch.full(shape, float("nan"), dtype=data.dtype, device="cuda")
+    x[shape[0] - 1] = data[0].cuda()
+    return x
+
+
+@pytest.mark.parametrize("kernel", PREFILL_KERNELS + ["split", "f32"])
+def test_prefill_kv_past_2g_elements(kernel, monkeypatch):
+    # 129 sequences of 65536 keys: the last sequence's K and V start at element 2^31
+    dt = "f32" if kernel == "f32" else "bf16"
+    B, Hq, Hkv, ql, kl, D = (129, 2, 2, 64, 65536, 128) if dt == "f32" else (129, 8, 2, 64, 65536, 128)
+    assert (B - 1) * Hkv * kl * D == BIG
+    if kernel in PREFILL_KERNELS:
+        monkeypatch.setenv("GQA_ATTN_PREFILL_KERNEL", kernel)
+    splits = 2 if kernel == "split" else 1
+    print(f"prefill K/V past 2^31 elements, kernel {kernel}", flush=True)
+    q1, k1, v1 = W.make_prefill(1, Hq, Hkv, ql, kl, D, dt, seed=131)
+    scale = W.fp32_scale(D)
+    q = _last_batch((B, Hq, ql, D), q1)
+    k = _last_batch((B, Hkv, kl, D), k1)
+    v = _last_batch((B, Hkv, kl, D), v1)
+    o, l = gqa.attn_fwd(q, k, v, causal=True, scale=scale, kv_splits=splits)
+    o_big, l_big = o[B - 1:].cpu(), l[B - 1:].cpu()
+    del q, k, v, o, l
+    _release()
+    o_small, l_small = gqa.attn_fwd(q1.cuda(), k1.cuda(), v1.cuda(), causal=True, scale=scale, kv_splits=splits)
+    assert torch.equal(o_big, o_small.cpu()) and torch.equal(l_big, l_small.cpu())
+    rows = sample_rows(1, Hq, ql, 64, 131)
+    o_ref, l_ref = oracle.attn_fwd(q1, k1, v1, scale, True, rows=rows)
+    check(o_big.double().numpy().reshape(-1, D)[rows], l_big.double().numpy().reshape(-1)[rows],
+          o_ref, l_ref, dt, f"K/V past 2^31, {kernel}")
+
+
+@pytest.mark.parametrize("kernel", PREFILL_KERNELS)
+def test_prefill_qo_past_2g_elements(kernel, monkeypatch):
+    # 1025 sequences x 8 heads x 2048 positions x 128 dims: the last sequence's
+    # Q and O rows start at element 2^31
+    B, Hq, Hkv, L, D = 1025, 8, 2, 2048, 128
+    assert (B - 1) * Hq * L * D == BIG
+    monkeypatch.setenv("GQA_ATTN_PREFILL_KERNEL", kernel)
+    print(f"prefill Q/O past 2^31 elements, kernel {kernel}", flush=True)
+    q1, k1, v1 = W.make_prefill(1, Hq, Hkv, L, L, D, "bf16", seed=1025)
+    scale = W.fp32_scale(D)
+    q = _last_batch((B, Hq, L, D), q1)
+    k = _last_batch((B, Hkv, L, D), k1)
+    v = _last_batch((B, Hkv, L, D), v1)
+    o, l = gqa.attn_fwd(q, k, v, causal=True, scale=scale, kv_splits=1)
+    o_big, l_big = o[B - 1:].cpu(), l[B - 1:].cpu()
+    del q, k, v, o, l
+    _release()
+    o_small, l_small = gqa.attn_fwd(q1.cuda(), k1.cuda(), v1.cuda(), causal=True, scale=scale, kv_splits=1)
+    assert torch.equal(o_big, o_small.cpu()) and torch.equal(l_big, l_small.cpu())
+    rows = sample_rows(1, Hq, L, 128, 1025)
+    o_ref, l_ref = oracle.attn_fwd(q1, k1, v1, scale, True, rows=rows)
+    check(o_big.double().numpy().reshape(-1, D)[rows], l_big.double().numpy().reshape(-1)[rows],
+          o_ref, l_ref, "bf16", f"Q/O past 2^31, {kernel}")
+
+
+def test_decode_pages_past_4gib():
+    # 256-token pages of 8 heads x 128 dims (512 KiB): page 8192 starts at element
+    # 2^31; every page the block table names sits at or above it
+    B, Hq, Hkv, D, ps, first = 4, 32, 8, 128, 256, 8192
+    assert first * ps * Hkv * D == BIG
+    scale = W.fp32_scale(D)
+    for q_len in (None, 4):
+        print(f"decode pages past 4 GiB, q_len {q_len}", flush=True)
+        inp = W.make_decode(B, Hq, Hkv, D, "bf16", seed=4096 + (q_len or 1), len_lo=300, len_hi=3000,
+                            page_size=ps, q_len=q_len)
+        big = W.DecodeInputs(inp.q, _pool(inp.k_cache, first, float("nan")), _pool(inp.v_cache, first, float("nan")),
+                             inp.seq_lens, _shift_table(inp.block_table, first), ps, inp.max_kv_len)
+        run = gpu_decode if q_len is None else gpu_decode_multi
+        o_big, l_big = run(big, 16, scale)
+        del big
+        _release()
+        o_small, l_small = run(inp, 16, scale)
+        assert np.array_equal(o_big, o_small) and np.array_equal(l_big, l_small)
+        if q_len is None:
+            o_ref, l_ref = oracle.attn_decode(inp.q, inp.k_cache, inp.v_cache, inp.seq_lens, scale,
+                                              block_table=inp.block_table, max_kv_len=inp.max_kv_len)
+        else:
+            o_ref, l_ref = oracle_multi(inp, scale)
+        check(o_big, l_big, o_ref, l_ref, "bf16", f"decode past 4 GiB, q_len {q_len}")
+
+
+def test_decode_fp8_pages_past_4gib():
+    # E4M3 pages of 256 tokens x 8 heads x 128 bytes (256 KiB): page 16384 starts
+    # at byte 2^32
+    B, Hq, Hkv, D, ps, first = 4, 32, 8, 128, 256, 16384
+    assert first * ps * Hkv * D == 2 * BIG
+    print("fp8 decode pages past 4 GiB", flush=True)
+    inp = W.make_decode_fp8(B, Hq, Hkv, D, "bf16", seed=16384, len_lo=300, len_hi=3000, page_size=ps)
+    scale = W.fp32_scale(D)
+    big = W.DecodeFp8Inputs(inp.q, _pool(inp.k8, first, NAN_E4M3), _pool(inp.v8, first, NAN_E4M3),
+                            _pool(inp.k_ss, first, NAN_SCALE_SHIFT), _pool(inp.v_ss, first, NAN_SCALE_SHIFT),
+                            inp.seq_lens, _shift_table(inp.block_table, first), ps, inp.max_kv_len)
+    o_big, l_big = gpu_decode_fp8(big, 16, scale)
+    del big
+    _release()
+    o_small, l_small = gpu_decode_fp8(inp, 16, scale)
+    assert np.array_equal(o_big, o_small) and np.array_equal(l_big, l_small)
+    o_ref, l_ref = oracle_fp8(inp, scale)
+    check(o_big, l_big, o_ref, l_ref, "bf16", "fp8 decode past 4 GiB")
+
+
+@pytest.mark.parametrize("kernel", PREFILL_KERNELS)
+def test_prefill_paged_pages_past_4gib(kernel, monkeypatch):
+    # paged prefill over 256-token pages of 8 heads x 128 dims: every page of
+    # the batch at or above page 8192 (element 2^31)
+    Hq, Hkv, D, ps, first = 32, 8, 128, 256, 8192
+    monkeypatch.setenv("GQA_ATTN_PREFILL_KERNEL", kernel)
+    print(f"paged prefill pages past 4 GiB, kernel {kernel}", flush=True)
+    inp = W.make_paged_prefill(3, Hq, Hkv, D, "bf16", seed=8192, q_lo=1, q_hi=300, prefix_lo=0, prefix_hi=700,
+                               page_size=ps)
+    scale = W.fp32_scale(D)
+    big = W.PagedPrefillInputs(inp.q, _pool(inp.k_cache, first, float("nan")),
+                               _pool(inp.v_cache, first, float("nan")), inp.qo_indptr, inp.kv_indptr,
+                               _shift_table(inp.kv_indices, first), inp.kv_last_page_len, ps, inp.max_q_len)
+    o_big, l_big = gpu_prefill_paged(big, True, scale)
+    del big
+    _release()
+    o_small, l_small = gpu_prefill_paged(inp, True, scale)
+    assert np.array_equal(o_big, o_small) and np.array_equal(l_big, l_small)
+    o_ref, l_ref = oracle_prefill_paged(inp, True, scale)
+    check(o_big, l_big, o_ref, l_ref, "bf16", f"paged prefill past 4 GiB, {kernel}")
