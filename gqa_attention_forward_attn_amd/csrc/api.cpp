@@ -89,7 +89,7 @@ int attn_fwd_kv_splits(int B, int Hq, int Hkv, int q_len, int kv_len, int D, int
     // of workgroups costs more than the idle CUs it would fill)
     const long long items = gqa::prefill_pp_items(B, Hq, Hkv, q_len);
     long long splits = n_cu / items;
-    const long long max_by_keys = kv_len / 1024;  // at least 16 key tiles per range
+    const long long max_by_keys = kv_len / 512;  // at least 8 key tiles per range
     if (splits > max_by_keys) splits = max_by_keys;
     if (splits > 8) splits = 8;
     return splits < 2 ? 1 : (int)splits;
