@@ -75,7 +75,6 @@ gqa_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, floa
 }
 
 int attn_fwd_kv_splits(int B, int Hq, int Hkv, int q_len, int kv_len, int D, int causal, gqa_dtype_t dtype) {
-    (void)causal;
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || q_len <= 0 || kv_len <= 0 || Hq % Hkv != 0) return 1;
     if (!supported_head_dim(D) || (dtype != GQA_BF16 && dtype != GQA_F16)) return 1;
     // Only where the ping-pong kernel would leave at least half of the CUs idle,
@@ -85,10 +84,14 @@ int attn_fwd_kv_splits(int B, int Hq, int Hkv, int q_len, int kv_len, int D, int
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
         return 1;
-    // as many ranges as fit one workgroup per CU (rounded down: a second round
-    // of workgroups costs more than the idle CUs it would fill)
+    // as many ranges as fit one workgroup per CU (rounded down: for blocks of
+    // similar length a second round costs more than the idle CUs it would fill)
     const long long items = gqa::prefill_pp_items(B, Hq, Hkv, q_len);
     long long splits = n_cu / items;
+    // causal with an offset below q_len: the blocks' key counts run from a few
+    // tiles to all of them, and twice the ranges (a second, shorter round that
+    // the longest-first order packs behind the long pieces) balances better
+    if (causal && kv_len - q_len < q_len && splits >= 2) splits *= 2;
     const long long max_by_keys = kv_len / 512;  // at least 8 key tiles per range
     if (splits > max_by_keys) splits = max_by_keys;
     if (splits > 8) splits = 8;

@@ -133,7 +133,8 @@ gqa_status_t attn_fwd_split(const void* q, const void* k, const void* v, void* o
  * attn_fwd_kv_splits - the key-range count the library recommends for
  * attn_fwd_split on this shape on the current device: for F16/BF16 with
  * kv_len >= 2048, as many ranges as fit one workgroup of 256 (query, head) rows
- * per compute unit (CU count / blocks of rows, rounded down; at most
+ * per compute unit (CU count / blocks of rows, rounded down, and twice that
+ * for causal shapes with kv_len - q_len < q_len when it is at least 2; at most
  * kv_len / 512 so that each range keeps >= 8 key tiles, at most 8); 1 when
  * that is 1 or the shape does not qualify (call attn_fwd).  Host-only; reads
  * the device's CU count.
