@@ -44,9 +44,9 @@ METRIC = "attention fwd TFLOP/s + % bf16 MFMA peak; decode GB/s + % HBM peak"
 # other source reports traffic null.
 TRAFFIC_MEASUREMENT = {
     "source": "gqa_attention_forward_attn_amd/csrc/prefill_pp.hip",
-    "sha1": "63b14774f51d3b92a42b64f075be1d0e2669d24f",
-    "fetch_kib": 25018.6, "write_kib": 33280.0,
-    "copy_fetch_kib": 262156.0, "copy_write_kib": 524288.0,
+    "sha1": "9ba494846a29ff65bfdebb91d2477b01ce562182",
+    "fetch_kib": 24791.2, "write_kib": 33280.0,
+    "copy_fetch_kib": 262156.3, "copy_write_kib": 524288.0,
 }
 
 

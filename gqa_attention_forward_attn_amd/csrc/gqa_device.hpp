@@ -171,4 +171,80 @@ __device__ __forceinline__ u32x4 ld_global_16(const void* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Sum over the wave of per-lane values in [0, 2^nbits): one ballot per bit.
+__device__ __forceinline__ int wave_sum_bits(int v, int nbits) {
+    int s = 0;
+    for (int j = 0; j < nbits; ++j)
+        s += __builtin_popcountll(__builtin_amdgcn_ballot_w64(((v >> j) & 1) != 0)) << j;
+    return s;
+}
+
+// Work order of a ragged prefill batch over a paged cache (at most 512
+// requests: one lane per request in each of 8 chunks of 64).  Item (b, i) is
+// request b's i-th block of POS query rows counted from its last query, so its
+// rows see at most kv_b - i * POS keys.  Items go in the order of their level
+// s_b + i, s_b = (kref - kv_b) / POS with kref = the pages of the whole batch
+// times the page size (>= every kv_b), ties in request order: the longest
+// blocks of the whole batch come first, and the in-order dispatch of
+// workgroups ends on short ones.  Returns the request of item `item` and sets
+// `i`, or returns -1 past the last item.  The answer is wave-uniform and the
+// same in every wave of a workgroup.
+template <int POS>
+__device__ int ragged_item(const int* qo_indptr, const int* kv_indptr, const int* kv_last_page_len,
+                           int page_shift, int B, int n_pos_tiles, int item, int& i) {
+    const int lane = __lane_id();
+    const int n_chunks = (B + 63) / 64;
+    const long long kref = (long long)(kv_indptr[B] - kv_indptr[0]) << page_shift;
+    int npt[8], lvl[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const int r = c * 64 + lane;
+        int nq = 0;
+        long long kv = 0;
+        if (r < B) {
+            nq = qo_indptr[r + 1] - qo_indptr[r];
+            const int np = kv_indptr[r + 1] - kv_indptr[r];
+            if (np > 0)
+                kv = ((long long)(np - 1) << page_shift) +
+                     (kv_last_page_len ? kv_last_page_len[r] : (1 << page_shift));
+        }
+        npt[c] = (nq + POS - 1) / POS;
+        lvl[c] = (int)((kref - kv) / POS);
+    }
+    // a lane's count is at most 8 * n_pos_tiles
+    const int nbits = 35 - __builtin_clz((unsigned)(n_pos_tiles > 0 ? n_pos_tiles : 1));
+    auto upto = [&](int L) {  // items at levels <= L
+        int v = 0;
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            if (c < n_chunks) v += min(max(L + 1 - lvl[c], 0), npt[c]);
+        return wave_sum_bits(v, nbits);
+    };
+    const int lend = (int)(kref / POS) + n_pos_tiles;  // every level is below lend
+    if (item >= upto(lend - 1)) return -1;
+    int lo = 0, hi = lend - 1;  // the level of the item: the first L with upto(L) > item
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (upto(mid) > item) hi = mid;
+        else lo = mid + 1;
+    }
+    int k = item - (lo > 0 ? upto(lo - 1) : 0);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        if (c >= n_chunks) break;
+        const bool has = lvl[c] <= lo && lo < lvl[c] + npt[c];
+        const uint64_t m = __builtin_amdgcn_ballot_w64(has);
+        const int cnt = __builtin_popcountll(m);
+        if (k < cnt) {
+            // the k-th request (in index order) of this chunk with a block at level lo
+            const int rank = __builtin_popcountll(m & ((1ull << lane) - 1ull));
+            const int sel = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(has && rank == k));
+            i = lo - __builtin_amdgcn_readlane(lvl[c], sel);
+            return c * 64 + sel;
+        }
+        k -= cnt;
+    }
+    return -1;
+}
+
 }  // namespace gqa

@@ -72,41 +72,16 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_mfma(PrefillArgs a) {
     int pt, hg, g, b;
     bool from_end = false;  // PAGED: position tile counted from the request's last query
     if (PAGED && a.B <= 512) {
-        // Ragged batch: only real items, in the order (i, request) with i the
-        // position tile counted from the request's end, heads fastest; the
-        // grid's surplus workgroups come last (as in prefill_pp.hip).
+        // Ragged batch: only real items, longest first across the whole batch
+        // (ragged_item), heads fastest; the grid's surplus workgroups come last
+        // (as in prefill_pp.hip).
         const int n_hk = a.Hkv * hgroups;
         int item = blockIdx.x / n_hk;
         const int hk = blockIdx.x - item * n_hk;
         hg = hk % hgroups;
         g = hk / hgroups;
-        // position tiles of requests c * 64 + lane (c < 8), kept in registers
-        int npt[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const int r = c * 64 + lane;
-            const int nq = r < a.B ? a.qo_indptr[r + 1] - a.qo_indptr[r] : 0;
-            npt[c] = (nq + POS - 1) / POS;
-        }
-        const int n_chunks = (a.B + 63) / 64;
-        b = -1;
-        pt = 0;
-        for (int i = 0; i < a.n_pos_tiles && b < 0; ++i) {
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                if (c >= n_chunks || b >= 0) break;
-                const uint64_t has = __builtin_amdgcn_ballot_w64(npt[c] > i);
-                const int cnt = __builtin_popcountll(has);
-                if (item < cnt) {
-                    // the item-th request (in index order) of this chunk that has an i-th tile
-                    const int rank = __builtin_popcountll(has & ((1ull << lane) - 1ull));
-                    b = c * 64 + (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(npt[c] > i && rank == item));
-                    pt = i;
-                } else {
-                    item -= cnt;
-                }
-            }
-        }
+        b = ragged_item<POS>(a.qo_indptr, a.kv_indptr, a.kv_last_page_len, a.page_shift, a.B, a.n_pos_tiles,
+                             item, pt);
         if (b < 0) return;  // workgroup-uniform, before any barrier: no item left
         from_end = true;
     } else {

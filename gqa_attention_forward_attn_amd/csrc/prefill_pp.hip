@@ -149,43 +149,18 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
     int pt, hg, g, b;
     bool from_end = false;  // PAGED: position tile counted from the request's last query
     if (PAGED && a.B <= 512) {
-        // Ragged batch: workgroups in order of (i, request), i = position tile
-        // counted from each request's end (its rows see the most keys), over the
-        // requests that have an i-th tile; the heads fastest.  Workgroups past
-        // the last such item (the grid is sized by the longest request) come
-        // last and exit, so that they do not hold up the dispatch of real work.
+        // Ragged batch: only real items (request, position tile counted from the
+        // request's end), longest first across the whole batch (ragged_item),
+        // the heads fastest.  Workgroups past the last item (the grid is sized
+        // by the longest request) come last and exit, so that they do not hold
+        // up the dispatch of real work.
         const int n_hk = a.Hkv * hgroups;
         int item = id / n_hk;
         int hk = id - item * n_hk;
         hg = hk % hgroups;
         g = hk / hgroups;
-        // position tiles of requests c * 64 + lane (c < 8), kept in registers
-        int npt[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const int r = c * 64 + lane;
-            const int nq = r < a.B ? a.qo_indptr[r + 1] - a.qo_indptr[r] : 0;
-            npt[c] = (nq + POS - 1) / POS;
-        }
-        const int n_chunks = (a.B + 63) / 64;
-        b = -1;
-        pt = 0;
-        for (int i = 0; i < a.n_pos_tiles && b < 0; ++i) {
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                if (c >= n_chunks || b >= 0) break;
-                const uint64_t has = __builtin_amdgcn_ballot_w64(npt[c] > i);
-                const int cnt = __builtin_popcountll(has);
-                if (item < cnt) {
-                    // the item-th request (in index order) of this chunk that has an i-th tile
-                    const int rank = __builtin_popcountll(has & ((1ull << lane) - 1ull));
-                    b = c * 64 + (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(npt[c] > i && rank == item));
-                    pt = i;
-                } else {
-                    item -= cnt;
-                }
-            }
-        }
+        b = ragged_item<POS>(a.qo_indptr, a.kv_indptr, a.kv_last_page_len, a.page_shift, a.B, a.n_pos_tiles,
+                             item, pt);
         if (b < 0) return;  // workgroup-uniform, before any barrier: no item left
         from_end = true;
     } else {
