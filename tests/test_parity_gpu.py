@@ -442,6 +442,8 @@ PAGED_PREFILL = [
     (16, 2, 128, "f16", 4, True, ([200, 64, 7, 130], [150, 64, 3, 400])),  # some q_len > kv_len
     (8, 2, 128, "bf16", 16, True, (70, (1, 40), (0, 60))),       # > 64 requests (work order over 2 lane chunks)
     (4, 2, 64, "bf16", 16, True, (520, (1, 8), (0, 12))),        # > 512 requests: the dense work order
+    (8, 2, 128, "bf16", 8, True, (300, (1, 70), (0, 900))),      # 5 chunks of requests, prefixes 0-900: long-first order
+    (8, 4, 64, "f16", 32, False, (100, (1, 130), (0, 400))),     # non-causal over 2 chunks
 ]
 
 
