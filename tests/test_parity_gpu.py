@@ -116,6 +116,35 @@ def test_prefill_split_all_elements(case, monkeypatch):
     assert float((o.float() - o1.float()).abs().max()) <= 1.6e-2
 
 
+
+# small grids at full length: the library's own range count (2 x the CUs /
+# blocks for causal shapes whose offset is below q_len, ranges of >= 8 tiles)
+RECOMMENDED_SPLIT = [
+    # B, Hq, Hkv, q_len, kv_len
+    (2, 4, 1, 2048, 2048),     # one GPU's share of the 2 x 32-head workload over 8 GPUs
+    (1, 8, 2, 3072, 3072),     # causal without offset: the doubled count
+    (1, 32, 4, 512, 4096),     # offset 3584 >= q_len: not doubled
+]
+
+
+@pytest.mark.parametrize("shape", RECOMMENDED_SPLIT, ids=lambda c: "-".join(map(str, c)))
+def test_prefill_recommended_split_small_grid(shape, monkeypatch):
+    B, Hq, Hkv, Lq, Lk = shape
+    S = gqa.lib().attn_fwd_kv_splits(B, Hq, Hkv, Lq, Lk, 128, 1, gqa._TORCH_DT[torch.bfloat16])
+    print(f"recommended split {shape}: {S} ranges", flush=True)
+    assert S >= 2
+    q, k, v = W.make_prefill(B, Hq, Hkv, Lq, Lk, 128, "bf16", seed=Lq + Lk + Hq)
+    scale = W.fp32_scale(128)
+    o, l = gpu_fwd(q, k, v, True, scale, kv_splits=None)
+    rows = sample_rows(B, Hq, Lq, 512, Lq + Hq)
+    o_ref, l_ref = oracle.attn_fwd(q, k, v, scale, True, rows=rows)
+    check(o.double().cpu().numpy().reshape(-1, 128)[rows], l.double().cpu().numpy().reshape(-1)[rows],
+          o_ref, l_ref, "bf16", str(shape))
+    monkeypatch.setenv("GQA_ATTN_PREFILL_KERNEL", "pingpong")
+    o1, l1 = gpu_fwd(q, k, v, True, scale, kv_splits=1)
+    assert float((l.cpu() - l1.cpu()).abs().max()) <= 1e-5
+    assert float((o.float() - o1.float()).abs().max()) <= 1.6e-2
+
 def test_prefill_kv_len_zero():
     q = torch.randn(1, 4, 16, 64).to(torch.bfloat16)
     k = torch.zeros(1, 2, 0, 64, dtype=torch.bfloat16)
