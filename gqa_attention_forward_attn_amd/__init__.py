@@ -158,6 +158,9 @@ def attn_prefill_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
         if t.dtype != torch.int32 or not t.is_contiguous():
             raise TypeError("index arrays must be contiguous int32 tensors")
     B = qo_indptr.numel() - 1
+    if _checking_tables():
+        check_paged_prefill_tables(qo_indptr, kv_indptr, kv_indices, kv_last_page_len, k_cache.shape[0],
+                                   page_size, int(max_q_len), total_q)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -169,6 +172,71 @@ def attn_prefill_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
                                   _stream(q.device))
     _check("attn_prefill_paged", rc)
     return out, lse
+
+
+# ---- host-side checks of the tables the kernels trust --------------------------
+# The kernels read sequence lengths, block tables and CSR pointers without
+# bounds checks (an out-of-range page id is undefined behaviour).  These checks
+# copy the tables to the host (a synchronising copy) and raise ValueError at the
+# first entry a kernel would read out of range.  They run before every launch
+# when GQA_ATTN_CHECK_TABLES=1, and can be called directly.
+
+def _host_ints(t: torch.Tensor):
+    return t.detach().to("cpu", torch.int64).reshape(-1).tolist()
+
+
+def check_decode_tables(seq_lens: torch.Tensor, block_table: Optional[torch.Tensor], page_size: int,
+                        num_pages: int, max_kv_len: int) -> None:
+    """seq_lens [B]: 0 <= len <= max_kv_len.  block_table [B, max_pages] (paged):
+    the ceil(len / page_size) entries of row b that the kernels read lie in
+    [0, num_pages) and fit the row."""
+    lens = _host_ints(seq_lens)
+    for b, n in enumerate(lens):
+        if n < 0 or n > max_kv_len:
+            raise ValueError(f"seq_lens[{b}] = {n} outside [0, {max_kv_len}]")
+    if block_table is None:
+        return
+    max_pages = block_table.shape[1]
+    rows = block_table.detach().to("cpu", torch.int64)
+    for b, n in enumerate(lens):
+        used = (n + page_size - 1) // page_size
+        if used > max_pages:
+            raise ValueError(f"sequence {b} needs {used} pages, the block table has {max_pages} per row")
+        for j, pg in enumerate(rows[b, :used].tolist()):
+            if pg < 0 or pg >= num_pages:
+                raise ValueError(f"block_table[{b}, {j}] = {pg} outside [0, {num_pages})")
+
+
+def check_paged_prefill_tables(qo_indptr: torch.Tensor, kv_indptr: torch.Tensor, kv_indices: torch.Tensor,
+                               kv_last_page_len: Optional[torch.Tensor], num_pages: int, page_size: int,
+                               max_q_len: int, total_q: int) -> None:
+    """CSR pointers non-decreasing from 0, within their arrays; every request's
+    query count <= max_q_len; page ids in [0, num_pages); a request with pages
+    has 1 <= kv_last_page_len <= page_size."""
+    qo, kvp, idx = _host_ints(qo_indptr), _host_ints(kv_indptr), _host_ints(kv_indices)
+    B = len(qo) - 1
+    if len(kvp) != B + 1:
+        raise ValueError("qo_indptr and kv_indptr must have the same length")
+    if qo[0] != 0 or kvp[0] != 0:
+        raise ValueError("qo_indptr[0] and kv_indptr[0] must be 0")
+    if qo[-1] > total_q or kvp[-1] > len(idx):
+        raise ValueError("the pointers run past q or kv_indices")
+    last = None if kv_last_page_len is None else _host_ints(kv_last_page_len)
+    for b in range(B):
+        nq, npg = qo[b + 1] - qo[b], kvp[b + 1] - kvp[b]
+        if nq < 0 or npg < 0:
+            raise ValueError(f"request {b}: decreasing pointers")
+        if nq > max_q_len:
+            raise ValueError(f"request {b}: {nq} queries > max_q_len = {max_q_len}")
+        if npg > 0 and last is not None and not 1 <= last[b] <= page_size:
+            raise ValueError(f"kv_last_page_len[{b}] = {last[b]} outside [1, {page_size}]")
+    for j, pg in enumerate(idx[:kvp[-1]]):
+        if pg < 0 or pg >= num_pages:
+            raise ValueError(f"kv_indices[{j}] = {pg} outside [0, {num_pages})")
+
+
+def _checking_tables() -> bool:
+    return os.environ.get("GQA_ATTN_CHECK_TABLES") == "1"
 
 
 def decode_workspace_bytes(B: int, Hq: int, D: int, n_splits: int) -> int:
@@ -212,6 +280,8 @@ def attn_decode_splitk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_le
     B, Hq, D = q.shape
     Hkv, page_size, max_pages, max_kv_len = _decode_layout(k, block_table, max_kv_len)
     _decode_checks(q, k, v, seq_lens)
+    if _checking_tables():
+        check_decode_tables(seq_lens, block_table, page_size, k.shape[0], max_kv_len)
     need = decode_workspace_bytes(B, Hq, D, n_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
@@ -241,6 +311,8 @@ def attn_decode_splitk_fp8(q: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, 
     scale in bits 0-15, shift in bits 16-31).  Returns (o [B,Hq,D], lse [B,Hq])."""
     B, Hq, D = q.shape
     Hkv, page_size, max_pages, max_kv_len = _decode_layout(k8, block_table, max_kv_len)
+    if _checking_tables():
+        check_decode_tables(seq_lens, block_table, page_size, k8.shape[0], max_kv_len)
     if seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous():
         raise TypeError("seq_lens must be a contiguous int32 tensor")
     if q.dtype not in (torch.bfloat16, torch.float16):
@@ -285,6 +357,8 @@ def attn_decode_splitk_multi(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, 
     B, Hq, q_len, D = q.shape
     Hkv, page_size, max_pages, max_kv_len = _decode_layout(k, block_table, max_kv_len)
     _decode_checks(q, k, v, seq_lens)
+    if _checking_tables():
+        check_decode_tables(seq_lens, block_table, page_size, k.shape[0], max_kv_len)
     need = decode_workspace_bytes_multi(B, Hq, q_len, D, n_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)

@@ -5,6 +5,8 @@ Tolerances (max abs error over the compared elements):
   bf16 / fp16 inputs  O within 2e-2, LSE within 1e-3
 A -inf LSE must be -inf on both sides and no NaN may appear anywhere.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -14,6 +16,10 @@ import gqa_attention_forward_attn_amd as gqa
 import workloads as W
 
 pytestmark = pytest.mark.gpu
+
+# every block table and CSR pointer set a test passes is also checked on the
+# host before the launch (the kernels themselves trust them)
+os.environ["GQA_ATTN_CHECK_TABLES"] = "1"
 
 TOL = {"f32": (1e-5, 1e-5), "bf16": (2e-2, 1e-3), "f16": (2e-2, 1e-3)}
 DTNAME = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16"}
