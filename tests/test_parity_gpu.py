@@ -393,6 +393,8 @@ DECODE_MULTI = [
     (5, 4, 2, 64, "f16", 16, 1, 63, 1, 1),            # page size 1; some sequences shorter than q_len
     (2, 6, 3, 64, "bf16", 3, 500, 900, 128, 7),       # 6 columns
     (3, 32, 4, 128, "bf16", 5, 1, 200, 16, 16),       # 40 columns: a ragged last block; many empty splits
+    (2, 8, 2, 128, "bf16", 256, 300, 900, 64, 8),     # q_len at its maximum: 1024 columns, 64 blocks
+    (2, 4, 4, 64, "f16", 256, 1, 300, 16, 4),         # maximum q_len over sequences shorter than it
 ]
 
 
