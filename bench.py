@@ -91,8 +91,10 @@ def time_launches(fn, steps: int, warmup: int):
     """Warm up, then time `steps` back-to-back calls: wall time around the loop
     (synchronize on both sides) and one HIP event pair around it on the stream
     the library launches on (torch's current stream), whose span / steps is the
-    mean launch duration.  A second pass with an event pair around every call
-    gives the spread (min, p90); those pairs also hold the dispatch gap."""
+    mean launch duration (`kernel_ms_mean`).  A second pass records an event
+    pair around every single call: those spans (`call_span_ms_min`,
+    `call_span_ms_p90`) also hold each call's own dispatch gap, so they are
+    longer than the back-to-back mean and describe the spread only."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -138,8 +140,8 @@ def bench_prefill(spec, steps, warmup):
                   "kv_len": spec.kv_len, "D": spec.D},
         "flop_per_launch": flops,
         "ms_per_step": wall / steps * 1e3,
-        "kernel_ms_mean": kern_s * 1e3, "kernel_ms_min": float(per.min()) * 1e3,
-        "kernel_ms_p90": float(np.percentile(per, 90)) * 1e3,
+        "kernel_ms_mean": kern_s * 1e3, "call_span_ms_min": float(per.min()) * 1e3,
+        "call_span_ms_p90": float(np.percentile(per, 90)) * 1e3,
         "tflops": flops * steps / wall / 1e12,
         "kernel_tflops": flops / kern_s / 1e12,
         "peak_tflops": peak,
@@ -176,7 +178,7 @@ def bench_decode_fp8(spec, steps, warmup):
         "bytes_per_step": nbytes,
         "workspace_bytes_rw": 2 * spec.B * spec.Hq * spec.n_splits * (spec.D + 1) * 4,
         "ms_per_step": wall / steps * 1e3,
-        "kernel_ms_mean": kern_s * 1e3, "kernel_ms_min": float(per.min()) * 1e3,
+        "kernel_ms_mean": kern_s * 1e3, "call_span_ms_min": float(per.min()) * 1e3,
         "gbps": nbytes * steps / wall / 1e9,
         "kernel_gbps": nbytes / kern_s / 1e9,
         "tokens_per_s": tokens / kern_s,
@@ -212,7 +214,7 @@ def bench_paged_prefill(spec, steps, warmup):
                   "total_q": int(sum(q_lens)), "sum_kv_len": int(sum(kv_lens))},
         "flop_per_launch": flops,
         "ms_per_step": wall / steps * 1e3,
-        "kernel_ms_mean": kern_s * 1e3, "kernel_ms_min": float(per.min()) * 1e3,
+        "kernel_ms_mean": kern_s * 1e3, "call_span_ms_min": float(per.min()) * 1e3,
         "tflops": flops * steps / wall / 1e12,
         "kernel_tflops": flops / kern_s / 1e12,
         "peak_tflops": PEAK_MFMA_16BIT_TFLOPS,
@@ -258,7 +260,7 @@ def bench_decode(spec, steps, warmup):
         "bytes_per_step": nbytes,
         "workspace_bytes_rw": 2 * spec.B * spec.Hq * spec.q_len * spec.n_splits * (spec.D + 1) * 4,
         "ms_per_step": wall / steps * 1e3,
-        "kernel_ms_mean": kern_s * 1e3, "kernel_ms_min": float(per.min()) * 1e3,
+        "kernel_ms_mean": kern_s * 1e3, "call_span_ms_min": float(per.min()) * 1e3,
         "gbps": nbytes * steps / wall / 1e9,
         "kernel_gbps": nbytes / kern_s / 1e9,
         "peak_gbps": PEAK_HBM_GBPS,
@@ -266,35 +268,125 @@ def bench_decode(spec, steps, warmup):
     }
 
 
-def cpu_baseline(spec, target_s=12.0):
-    """The oracle, as it stands, on an evenly spaced sample of rows of the
-    workload; rate in TFLOP/s on the same visible-pair flop count."""
-    import oracle
-    q, k, v = W.make_prefill_spec(spec)
-    scale = W.fp32_scale(spec.D)
-    total = spec.B * spec.Hq * spec.q_len
-    delta = spec.kv_len - spec.q_len
+def _evenly(total: int, n: int) -> np.ndarray:
+    return np.unique(np.linspace(0, total - 1, max(1, min(total, n))).astype(np.int64))
 
-    def run(n):
-        rows = np.linspace(0, total - 1, n).astype(np.int64)
-        pos = rows % spec.q_len
+
+def _time_oracle(run_rows, total_rows, row_work, target_s, probe_n=256):
+    """Time the oracle on evenly spaced rows: a probe sizes the sample so that
+    it takes about target_s seconds.  Returns (work of the sampled rows,
+    seconds, rows sampled)."""
+    rows = _evenly(total_rows, probe_n)
+    t0 = time.perf_counter()
+    run_rows(rows)
+    dt = time.perf_counter() - t0
+    rows = _evenly(total_rows, int(probe_n * target_s / max(dt, 1e-3)))
+    t0 = time.perf_counter()
+    run_rows(rows)
+    dt = time.perf_counter() - t0
+    return row_work(rows), dt, len(rows)
+
+
+def cpu_baseline(spec, target_s=12.0):
+    """The oracle, as it stands, timed on the host's cores on a bounded sample
+    of the workload's rows (evenly spaced over all of them), its rate in the
+    workload's own unit: TFLOP/s on the visible-pair flop count (prefill) or
+    GB/s on the step's algorithmic bytes, prorated by the keys each sampled
+    row reads (decode)."""
+    import oracle
+    scale = W.fp32_scale(spec.D)
+    if isinstance(spec, W.DecodeSpec) or spec is W.FP8_PAGED_DECODE:
+        fp8 = spec is W.FP8_PAGED_DECODE
+        inp = W.make_decode_fp8_spec(spec) if fp8 else W.make_decode_spec(spec)
+        q_len = 1 if fp8 else spec.q_len
+        total = spec.B * spec.Hq * q_len
+        lens = inp.seq_lens.to(torch.int64).numpy()
+        row_len = lens[np.arange(total) // (spec.Hq * q_len)]
+        step_bytes = decode_bytes(spec, inp, fp8=fp8)
+
+        def run_rows(rows):
+            if fp8:
+                oracle.attn_decode_fp8(inp.q, inp.k8, inp.v8, inp.k_ss, inp.v_ss, inp.seq_lens, scale,
+                                       block_table=inp.block_table, max_kv_len=inp.max_kv_len, rows=rows)
+            elif q_len == 1:
+                oracle.attn_decode(inp.q, inp.k_cache, inp.v_cache, inp.seq_lens, scale,
+                                   block_table=inp.block_table, max_kv_len=inp.max_kv_len, rows=rows)
+            else:
+                oracle.attn_decode_multi(inp.q, inp.k_cache, inp.v_cache, inp.seq_lens, scale,
+                                         block_table=inp.block_table, max_kv_len=inp.max_kv_len, rows=rows)
+
+        work, dt, n = _time_oracle(run_rows, total, lambda r: step_bytes * row_len[r].sum() / row_len.sum(),
+                                   target_s)
+        value, unit = work / dt / 1e9, "GB/s"
+    elif isinstance(spec, W.PagedPrefillSpec):
+        inp = W.make_paged_prefill_spec(spec)
+        qo = inp.qo_indptr.to(torch.int64).numpy()
+        n_pages = (inp.kv_indptr[1:] - inp.kv_indptr[:-1]).to(torch.int64).numpy()
+        last = inp.kv_last_page_len.to(torch.int64).numpy()
+        kv = np.where(n_pages > 0, (n_pages - 1) * spec.page_size + last, 0)
+        tok = np.arange(qo[-1])
+        req = np.searchsorted(qo, tok, side="right") - 1
+        i = tok - qo[req]
+        qn = qo[req + 1] - qo[req]
+        vis = np.minimum(kv[req], np.maximum(0, i + 1 + kv[req] - qn)) if spec.causal else kv[req]
+        row_flops = np.repeat(4 * spec.D * vis, spec.Hq)   # flat row = token * Hq + head
+
+        def run_rows(rows):
+            oracle.attn_prefill_paged(inp.q, inp.k_cache, inp.v_cache, inp.qo_indptr, inp.kv_indptr,
+                                      inp.kv_indices, scale, spec.causal, inp.kv_last_page_len, rows=rows)
+
+        work, dt, n = _time_oracle(run_rows, len(row_flops), lambda r: row_flops[r].sum(), target_s)
+        total = len(row_flops)
+        value, unit = work / dt / 1e12, "TFLOP/s"
+    else:
+        q, k, v = W.make_prefill_spec(spec)
+        total = spec.B * spec.Hq * spec.q_len
+        pos = np.arange(total) % spec.q_len
+        delta = spec.kv_len - spec.q_len
         vis = np.minimum(spec.kv_len, np.maximum(0, pos + 1 + delta)) if spec.causal else \
             np.full_like(pos, spec.kv_len)
-        t0 = time.perf_counter()
-        oracle.attn_fwd(q, k, v, scale, spec.causal, rows=rows)
-        dt = time.perf_counter() - t0
-        return dt, int(4 * spec.D * vis.sum())
-
-    probe_n = 512
-    dt, _ = run(probe_n)
-    n = int(min(total, max(probe_n, probe_n * target_s / max(dt, 1e-3))))
-    dt, flops = run(n)
+        row_flops = 4 * spec.D * vis
+        work, dt, n = _time_oracle(lambda r: oracle.attn_fwd(q, k, v, scale, spec.causal, rows=r), total,
+                                   lambda r: row_flops[r].sum(), target_s)
+        value, unit = work / dt / 1e12, "TFLOP/s"
     return {
-        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-        "kind": "oracle",
-        "sample": f"{n} of {total} query rows of {spec.name} (evenly spaced), fp64, "
-                  f"{dt:.1f} s on {oracle.num_threads()} OpenMP threads ({platform.processor() or 'host CPU'})",
+        "value": value, "unit": unit, "cores": oracle.num_threads(), "kind": "oracle",
+        "sample": f"{n} of {total} rows of {spec.name} (evenly spaced), fp64, {dt:.1f} s on "
+                  f"{oracle.num_threads()} OpenMP threads ({platform.processor() or 'host CPU'})",
     }
+
+
+def _n_cu() -> int:
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def bench_mfma_ceiling(steps, warmup):
+    """The MFMA-only loop (include/gqa_ceilings.h) at the prefill kernel's
+    occupancy: the matrix-core rate the chip sustains under a full load."""
+    n_wg, iters = 4 * _n_cu(), 1000
+    out = torch.empty(n_wg * 512, dtype=torch.float32, device="cuda:0")
+    flops = gqa.ceiling_mfma(n_wg, iters, out)[0]
+    wall, kern_s, per = time_launches(lambda: gqa.ceiling_mfma(n_wg, iters, out), steps, warmup)
+    return {"workload": "mfma_ceiling", "what": "v_mfma_f32_32x32x16_bf16 back to back, 8 waves per CU, "
+            "no memory traffic", "flop_per_launch": flops, "kernel_ms_mean": kern_s * 1e3,
+            "tflops": flops / kern_s / 1e12, "peak_tflops": PEAK_MFMA_16BIT_TFLOPS,
+            "frac_of_peak": flops / kern_s / 1e12 / PEAK_MFMA_16BIT_TFLOPS}
+
+
+READ_CEILING_BYTES = 1 << 30
+
+
+def bench_read_ceiling(steps, warmup):
+    """The streaming read (include/gqa_ceilings.h) over 1 GiB, four times the
+    last-level cache: the rate HBM gives a pure read stream."""
+    src = torch.empty(READ_CEILING_BYTES // 4, dtype=torch.int32, device="cuda:0").random_()
+    n_wg = 32 * _n_cu()
+    out = torch.empty(n_wg, dtype=torch.int32, device="cuda:0")
+    wall, kern_s, per = time_launches(lambda: gqa.ceiling_stream_read(src, n_wg, out), steps, warmup)
+    return {"workload": "hbm_read_ceiling", "what": "16-byte non-temporal loads, every byte of 1 GiB once",
+            "bytes_per_launch": READ_CEILING_BYTES, "kernel_ms_mean": kern_s * 1e3,
+            "gbps": READ_CEILING_BYTES / kern_s / 1e9, "peak_gbps": PEAK_HBM_GBPS,
+            "frac_of_peak": READ_CEILING_BYTES / kern_s / 1e9 / PEAK_HBM_GBPS}
 
 
 def run_one(spec, steps, warmup):
@@ -329,8 +421,12 @@ def main():
     all_specs = [W.CAUSAL_GQA_FP32, W.CAUSAL_GQA_PREFILL, W.CAUSAL_GQA_OFFSET,
                  W.MHA_NONCAUSAL_FP16, W.PAGED_DECODE, W.FP8_PAGED_DECODE, W.MULTI_QUERY_DECODE,
                  W.RAGGED_PAGED_PREFILL]
+    ceilings = {"mfma_ceiling": bench_mfma_ceiling, "hbm_read_ceiling": bench_read_ceiling}
     if args.only == "hbm_copy":
         print(json.dumps(bench_copy(args.steps, args.warmup)), flush=True)
+        return
+    if args.only in ceilings:
+        print(json.dumps(ceilings[args.only](args.steps, args.warmup)), flush=True)
         return
     if args.only:
         specs = [s for s in all_specs if s.name == args.only]
@@ -347,6 +443,14 @@ def main():
         r = run_one(s, max(20, args.steps // 2), args.warmup)
         results[s.name] = r
         print(f"# {s.name}: {json.dumps(r)}", file=sys.stderr, flush=True)
+    ceil = {name: fn(20, 3) for name, fn in ceilings.items()}
+    print(f"# ceilings: {json.dumps(ceil)}", file=sys.stderr, flush=True)
+    mfma_ceil, read_ceil = ceil["mfma_ceiling"]["tflops"], ceil["hbm_read_ceiling"]["gbps"]
+    for r in results.values():
+        if "kernel_tflops" in r and r.get("dtype") != "f32":
+            r["frac_of_measured_mfma_ceiling"] = r["kernel_tflops"] / mfma_ceil
+        if "kernel_gbps" in r:
+            r["frac_of_measured_read_ceiling"] = r["kernel_gbps"] / read_ceil
 
     torch.cuda.synchronize()
     p = bench_prefill(PRIMARY, args.steps, args.warmup)
@@ -376,11 +480,18 @@ def main():
             "traffic": measured_traffic(),
             "kernel": "prefill_fwd_pp<bf16, D=128, causal, 4 heads/workgroup>",
             "kernel_ms_mean": round(p["kernel_ms_mean"], 5),
+            "measured_ceiling": {"value": round(mfma_ceil, 3), "unit": "TFLOP/s",
+                                 "what": ceil["mfma_ceiling"]["what"],
+                                 "frac": round(p["kernel_tflops"] / mfma_ceil, 4)},
         },
+        "ceilings": ceil,
         "workloads": results,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(PRIMARY)
+        for s in all_specs:
+            if s is not PRIMARY:
+                results[s.name]["cpu_baseline"] = cpu_baseline(s, target_s=3.0)
     print(json.dumps(line), flush=True)
 
 

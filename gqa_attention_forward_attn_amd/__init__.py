@@ -27,6 +27,12 @@ EXPORTS = ("attn_fwd", "attn_fwd_split", "attn_fwd_split_workspace_bytes", "attn
            "attn_prefill_paged", "attn_decode_workspace_bytes", "attn_decode_splitk",
            "attn_decode_splitk_fp8",
            "attn_decode_workspace_bytes_multi", "attn_decode_splitk_multi", "attn_status_str")
+# Every symbol include/gqa_attn_test.h declares (kernel selection for tests).
+TEST_EXPORTS = ("attn_fwd_with_kernel", "attn_prefill_paged_with_kernel")
+# Every symbol include/gqa_ceilings.h declares (measurement kernels).
+CEILING_EXPORTS = ("gqa_ceiling_mfma_flops", "gqa_ceiling_mfma", "gqa_ceiling_stream_read")
+# bf16 / fp16 prefill kernel names accepted by the `kernel` argument
+PREFILL_KERNELS = {None: 0, "auto": 0, "pingpong": 1, "fourwave": 2}
 
 _lib = None
 
@@ -49,6 +55,8 @@ def lib() -> ctypes.CDLL:
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32, vp]
     L.attn_fwd.restype = i32
+    L.attn_fwd_with_kernel.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32, i32, vp]
+    L.attn_fwd_with_kernel.restype = i32
     L.attn_fwd_split.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32, vp, sz, i32, vp]
     L.attn_fwd_split.restype = i32
     L.attn_fwd_split_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
@@ -58,6 +66,9 @@ def lib() -> ctypes.CDLL:
     L.attn_prefill_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                      f32, i32, i32, vp]
     L.attn_prefill_paged.restype = i32
+    L.attn_prefill_paged_with_kernel.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                                 i32, f32, i32, i32, i32, vp]
+    L.attn_prefill_paged_with_kernel.restype = i32
     L.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
     L.attn_decode_workspace_bytes.restype = sz
     L.attn_decode_splitk.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
@@ -71,6 +82,12 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_splitk_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                          i32, f32, i32, vp, sz, i32, vp]
     L.attn_decode_splitk_fp8.restype = i32
+    L.gqa_ceiling_mfma_flops.argtypes = [i32, i32]
+    L.gqa_ceiling_mfma_flops.restype = ctypes.c_longlong
+    L.gqa_ceiling_mfma.argtypes = [i32, i32, vp, vp]
+    L.gqa_ceiling_mfma.restype = i32
+    L.gqa_ceiling_stream_read.argtypes = [vp, sz, i32, vp, vp]
+    L.gqa_ceiling_stream_read.restype = i32
     L.attn_status_str.argtypes = [i32]
     L.attn_status_str.restype = ctypes.c_char_p
     _lib = L
@@ -94,33 +111,71 @@ def default_scale(D: int) -> float:
     return 1.0 / math.sqrt(D)
 
 
+# ---- argument checks: a tensor the kernels would read or write out of bounds
+# (wrong shape, device or layout) is refused here, before any launch ----------
+
+def _gpu_contig(name: str, t: torch.Tensor, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _int32_table(name: str, t: torch.Tensor, device):
+    _gpu_contig(name, t, device)
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be an int32 tensor")
+
+
+def _out_tensor(name: str, t: Optional[torch.Tensor], shape, dtype, device) -> torch.Tensor:
+    """A caller-given output must have exactly the shape and dtype the kernels write."""
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _gpu_contig(name, t, device)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} of shape {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+    return t
+
+
+def _kernel_code(kernel) -> int:
+    if kernel not in PREFILL_KERNELS:
+        raise ValueError(f"kernel must be one of {sorted(k for k in PREFILL_KERNELS if k)} or None")
+    return PREFILL_KERNELS[kernel]
+
+
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
              scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-             lse: Optional[torch.Tensor] = None, kv_splits: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+             lse: Optional[torch.Tensor] = None, kv_splits: Optional[int] = None,
+             kernel: Optional[str] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Attention forward. q [B,Hq,q_len,D], k/v [B,Hkv,kv_len,D] on one GPU.
 
     Returns (o [B,Hq,q_len,D] in q's dtype, lse [B,Hq,q_len] fp32, natural log).
     Causal masking is bottom-right aligned (query i sees keys j <= i + kv_len - q_len).
     kv_splits: key ranges per block of query rows (attn_fwd_split); None lets the
     library choose (attn_fwd_kv_splits), 1 forces the single-pass forward.
+    kernel: None / "auto" (by shape), "pingpong" or "fourwave" (bf16 / fp16
+    single pass; for tests that cover both kernels).
     """
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k/v must be 4-D: [B, H, len, D]")
     B, Hq, q_len, D = q.shape
     Bk, Hkv, kv_len, Dk = k.shape
     if Bk != B or Dk != D or tuple(v.shape) != tuple(k.shape):
         raise ValueError("shape mismatch between q, k and v")
     if q.dtype not in _TORCH_DT or k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share one dtype among float32/float16/bfloat16")
-    for t in (q, k, v):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("inputs must be contiguous GPU tensors")
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, Hq, q_len), dtype=torch.float32, device=q.device)
+    code = _kernel_code(kernel)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _gpu_contig(name, t, q.device)
+    out = _out_tensor("out", out, q.shape, q.dtype, q.device)
+    lse = _out_tensor("lse", lse, (B, Hq, q_len), torch.float32, q.device)
     sc = default_scale(D) if scale is None else float(scale)
     dt = _TORCH_DT[q.dtype]
     if kv_splits is None:
-        kv_splits = int(lib().attn_fwd_kv_splits(B, Hq, Hkv, q_len, kv_len, D, int(bool(causal)), dt))
+        kv_splits = 1 if code else int(lib().attn_fwd_kv_splits(B, Hq, Hkv, q_len, kv_len, D,
+                                                                 int(bool(causal)), dt))
     if kv_splits > 1:
         # small grids: key ranges in parallel, merged by LSE (workspace from torch's allocator)
         ws = torch.empty(int(lib().attn_fwd_split_workspace_bytes(B, Hq, q_len, D, kv_splits)),
@@ -129,6 +184,11 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = T
                                   sc, int(bool(causal)), int(kv_splits), _ptr(ws), ws.numel(), dt,
                                   _stream(q.device))
         _check("attn_fwd_split", rc)
+        return out, lse
+    if code:
+        rc = lib().attn_fwd_with_kernel(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, q_len,
+                                        kv_len, D, sc, int(bool(causal)), dt, code, _stream(q.device))
+        _check("attn_fwd_with_kernel", rc)
         return out, lse
     rc = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, q_len, kv_len, D,
                         sc, int(bool(causal)), dt, _stream(q.device))
@@ -140,36 +200,43 @@ def attn_prefill_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
                        qo_indptr: torch.Tensor, kv_indptr: torch.Tensor, kv_indices: torch.Tensor,
                        max_q_len: int, kv_last_page_len: Optional[torch.Tensor] = None, causal: bool = True,
                        scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-                       lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                       lse: Optional[torch.Tensor] = None,
+                       kernel: Optional[str] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Prefill of a batch of ragged requests over a paged KV cache.
 
     q [total_q, Hq, D] token-major; k/v_cache [num_pages, page_size, Hkv, D];
     qo_indptr, kv_indptr [B+1] int32; kv_indices int32 page ids; optional
     kv_last_page_len [B] int32.  `max_q_len` (a host int) must bound every
     request's query count.  Returns (o [total_q, Hq, D], lse [total_q, Hq] fp32).
+    kernel: None / "auto", "pingpong" or "fourwave" (as for attn_fwd).
     """
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [total_q, Hq, D] and the pool [num_pages, page_size, Hkv, D]")
     total_q, Hq, D = q.shape
     _, page_size, Hkv, Dk = k_cache.shape
     if Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape):
         raise ValueError("shape mismatch between q and the K/V pool")
     if q.dtype not in _TORCH_DT or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise TypeError("q and the K/V pool must share one dtype")
-    for t in (qo_indptr, kv_indptr, kv_indices) + (() if kv_last_page_len is None else (kv_last_page_len,)):
-        if t.dtype != torch.int32 or not t.is_contiguous():
-            raise TypeError("index arrays must be contiguous int32 tensors")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _gpu_contig(name, t, q.device)
+    for name, t in (("qo_indptr", qo_indptr), ("kv_indptr", kv_indptr), ("kv_indices", kv_indices)) + \
+            (() if kv_last_page_len is None else (("kv_last_page_len", kv_last_page_len),)):
+        _int32_table(name, t, q.device)
     B = qo_indptr.numel() - 1
-    if _checking_tables():
+    if kv_indptr.numel() != B + 1 or (kv_last_page_len is not None and kv_last_page_len.numel() != B):
+        raise ValueError("qo_indptr and kv_indptr need B + 1 entries, kv_last_page_len B")
+    code = _kernel_code(kernel)
+    if check_tables:
         check_paged_prefill_tables(qo_indptr, kv_indptr, kv_indices, kv_last_page_len, k_cache.shape[0],
                                    page_size, int(max_q_len), total_q)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((total_q, Hq), dtype=torch.float32, device=q.device)
+    out = _out_tensor("out", out, q.shape, q.dtype, q.device)
+    lse = _out_tensor("lse", lse, (total_q, Hq), torch.float32, q.device)
     sc = default_scale(D) if scale is None else float(scale)
-    rc = lib().attn_prefill_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), _ptr(qo_indptr),
-                                  _ptr(kv_indptr), _ptr(kv_indices), _ptr(kv_last_page_len), B, Hq, Hkv, D,
-                                  page_size, int(max_q_len), sc, int(bool(causal)), _TORCH_DT[q.dtype],
-                                  _stream(q.device))
+    rc = lib().attn_prefill_paged_with_kernel(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse),
+                                              _ptr(qo_indptr), _ptr(kv_indptr), _ptr(kv_indices),
+                                              _ptr(kv_last_page_len), B, Hq, Hkv, D, page_size, int(max_q_len),
+                                              sc, int(bool(causal)), _TORCH_DT[q.dtype], code, _stream(q.device))
     _check("attn_prefill_paged", rc)
     return out, lse
 
@@ -179,7 +246,8 @@ def attn_prefill_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
 # bounds checks (an out-of-range page id is undefined behaviour).  These checks
 # copy the tables to the host (a synchronising copy) and raise ValueError at the
 # first entry a kernel would read out of range.  They run before every launch
-# when GQA_ATTN_CHECK_TABLES=1, and can be called directly.
+# when `check_tables` is true (set from GQA_ATTN_CHECK_TABLES=1 when the module
+# is imported, or by set_check_tables), and can be called directly.
 
 def _host_ints(t: torch.Tensor):
     return t.detach().to("cpu", torch.int64).reshape(-1).tolist()
@@ -235,35 +303,67 @@ def check_paged_prefill_tables(qo_indptr: torch.Tensor, kv_indptr: torch.Tensor,
             raise ValueError(f"kv_indices[{j}] = {pg} outside [0, {num_pages})")
 
 
-def _checking_tables() -> bool:
-    return os.environ.get("GQA_ATTN_CHECK_TABLES") == "1"
+check_tables = os.environ.get("GQA_ATTN_CHECK_TABLES") == "1"
+
+
+def set_check_tables(on: bool) -> None:
+    """Check (or stop checking) every table on the host before each launch."""
+    global check_tables
+    check_tables = bool(on)
 
 
 def decode_workspace_bytes(B: int, Hq: int, D: int, n_splits: int) -> int:
     return int(lib().attn_decode_workspace_bytes(B, Hq, D, n_splits))
 
 
-def _decode_layout(k, block_table, max_kv_len):
+def _decode_geometry(q, k, v, seq_lens, block_table, max_kv_len, kv_dtype):
+    """Shapes of a decode call, checked against each other: q [B, Hq, (q_len,) D];
+    paged k/v [pages, page_size, Hkv, D] with block_table [B, max_pages], or dense
+    k/v [B, Hkv, L, D] (then max_kv_len, the row stride in tokens, must be L);
+    seq_lens [B].  Returns (Hkv, page_size, max_pages, max_kv_len)."""
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("q must be bfloat16 or float16")
+    if k.dtype != kv_dtype or v.dtype != kv_dtype:
+        raise TypeError(f"k and v must be {kv_dtype}")
+    if k.dim() != 4 or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be 4-D tensors of one shape")
+    B, D = q.shape[0], q.shape[-1]
+    if k.shape[3] != D:
+        raise ValueError(f"head dim of k ({k.shape[3]}) differs from q's ({D})")
+    if seq_lens.numel() != B:
+        raise ValueError(f"seq_lens has {seq_lens.numel()} entries for a batch of {B}")
     if block_table is not None:
+        if block_table.dim() != 2 or block_table.shape[0] != B:
+            raise ValueError("block_table must be [B, max_pages]")
         _, page_size, Hkv, _ = k.shape
         max_pages = block_table.shape[1]
         if max_kv_len is None:
             max_kv_len = max_pages * page_size
-        if block_table.dtype != torch.int32 or not block_table.is_contiguous():
-            raise TypeError("block_table must be a contiguous int32 tensor")
+        if not 0 <= int(max_kv_len) <= max_pages * page_size:
+            raise ValueError("max_kv_len must be within the block table's max_pages * page_size keys")
     else:
-        _, Hkv, L, _ = k.shape
+        Bk, Hkv, L, _ = k.shape
+        if Bk != B:
+            raise ValueError(f"dense k/v hold {Bk} sequences for a batch of {B}")
         page_size, max_pages = 0, 0
         if max_kv_len is None:
             max_kv_len = L
+        if int(max_kv_len) != L:
+            raise ValueError(f"dense layout: max_kv_len ({max_kv_len}) must equal k.shape[2] ({L}), "
+                             "the row stride in tokens")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _gpu_contig(name, t, q.device)
+    _int32_table("seq_lens", seq_lens, q.device)
+    if block_table is not None:
+        _int32_table("block_table", block_table, q.device)
     return Hkv, page_size, max_pages, int(max_kv_len)
 
 
-def _decode_checks(q, k, v, seq_lens):
-    if seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous():
-        raise TypeError("seq_lens must be a contiguous int32 tensor")
-    if q.dtype not in _TORCH_DT or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise TypeError("q, k, v must share one dtype")
+def _workspace(ws: Optional[torch.Tensor], need: int, device) -> torch.Tensor:
+    if ws is None:
+        return torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    _gpu_contig("workspace", ws, device)
+    return ws
 
 
 def attn_decode_splitk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens: torch.Tensor,
@@ -277,18 +377,15 @@ def attn_decode_splitk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_le
     Returns (o [B,Hq,D], lse [B,Hq] fp32).  `workspace` (uint8, >= decode_workspace_bytes)
     may be passed to avoid an allocation per call.
     """
+    if q.dim() != 3:
+        raise ValueError("q must be [B, Hq, D]")
     B, Hq, D = q.shape
-    Hkv, page_size, max_pages, max_kv_len = _decode_layout(k, block_table, max_kv_len)
-    _decode_checks(q, k, v, seq_lens)
-    if _checking_tables():
+    Hkv, page_size, max_pages, max_kv_len = _decode_geometry(q, k, v, seq_lens, block_table, max_kv_len, q.dtype)
+    if check_tables:
         check_decode_tables(seq_lens, block_table, page_size, k.shape[0], max_kv_len)
-    need = decode_workspace_bytes(B, Hq, D, n_splits)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    workspace = _workspace(workspace, decode_workspace_bytes(B, Hq, D, n_splits), q.device)
+    out = _out_tensor("out", out, q.shape, q.dtype, q.device)
+    lse = _out_tensor("lse", lse, (B, Hq), torch.float32, q.device)
     sc = default_scale(D) if scale is None else float(scale)
     rc = lib().attn_decode_splitk(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(seq_lens),
                                   _ptr(block_table), max_pages, page_size, B, Hq, Hkv, D,
@@ -309,26 +406,20 @@ def attn_decode_splitk_fp8(q: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, 
     [pages,page_size,Hkv,D] with block_table (page_size >= 16) or [B,Hkv,max_kv_len,D];
     k/v_scale_shift int32 [pages,page_size,Hkv] or [B,Hkv,max_kv_len] (binary16
     scale in bits 0-15, shift in bits 16-31).  Returns (o [B,Hq,D], lse [B,Hq])."""
+    if q.dim() != 3:
+        raise ValueError("q must be [B, Hq, D]")
     B, Hq, D = q.shape
-    Hkv, page_size, max_pages, max_kv_len = _decode_layout(k8, block_table, max_kv_len)
-    if _checking_tables():
+    Hkv, page_size, max_pages, max_kv_len = _decode_geometry(q, k8, v8, seq_lens, block_table, max_kv_len,
+                                                             torch.uint8)
+    for name, t in (("k_scale_shift", k_scale_shift), ("v_scale_shift", v_scale_shift)):
+        if tuple(t.shape) != tuple(k8.shape[:3]):
+            raise ValueError(f"{name} must be {tuple(k8.shape[:3])} (one word per token row and head)")
+        _int32_table(name, t, q.device)
+    if check_tables:
         check_decode_tables(seq_lens, block_table, page_size, k8.shape[0], max_kv_len)
-    if seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous():
-        raise TypeError("seq_lens must be a contiguous int32 tensor")
-    if q.dtype not in (torch.bfloat16, torch.float16):
-        raise TypeError("q must be bfloat16 or float16")
-    if k8.dtype != torch.uint8 or v8.dtype != torch.uint8:
-        raise TypeError("the E4M3 cache is passed as uint8 bytes")
-    for t in (k_scale_shift, v_scale_shift):
-        if t.dtype != torch.int32 or not t.is_contiguous():
-            raise TypeError("scale-shift words must be contiguous int32 tensors")
-    need = decode_workspace_bytes(B, Hq, D, n_splits)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    workspace = _workspace(workspace, decode_workspace_bytes(B, Hq, D, n_splits), q.device)
+    out = _out_tensor("out", out, q.shape, q.dtype, q.device)
+    lse = _out_tensor("lse", lse, (B, Hq), torch.float32, q.device)
     sc = default_scale(D) if scale is None else float(scale)
     rc = lib().attn_decode_splitk_fp8(_ptr(q), _ptr(k8), _ptr(v8), _ptr(k_scale_shift), _ptr(v_scale_shift),
                                       _ptr(out), _ptr(lse), _ptr(seq_lens), _ptr(block_table), max_pages,
@@ -354,18 +445,15 @@ def attn_decode_splitk_multi(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, 
     q [B,Hq,q_len,D]; k/v and block_table as for attn_decode_splitk.
     Returns (o [B,Hq,q_len,D], lse [B,Hq,q_len] fp32).
     """
+    if q.dim() != 4:
+        raise ValueError("q must be [B, Hq, q_len, D]")
     B, Hq, q_len, D = q.shape
-    Hkv, page_size, max_pages, max_kv_len = _decode_layout(k, block_table, max_kv_len)
-    _decode_checks(q, k, v, seq_lens)
-    if _checking_tables():
+    Hkv, page_size, max_pages, max_kv_len = _decode_geometry(q, k, v, seq_lens, block_table, max_kv_len, q.dtype)
+    if check_tables:
         check_decode_tables(seq_lens, block_table, page_size, k.shape[0], max_kv_len)
-    need = decode_workspace_bytes_multi(B, Hq, q_len, D, n_splits)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, Hq, q_len), dtype=torch.float32, device=q.device)
+    workspace = _workspace(workspace, decode_workspace_bytes_multi(B, Hq, q_len, D, n_splits), q.device)
+    out = _out_tensor("out", out, q.shape, q.dtype, q.device)
+    lse = _out_tensor("lse", lse, (B, Hq, q_len), torch.float32, q.device)
     sc = default_scale(D) if scale is None else float(scale)
     rc = lib().attn_decode_splitk_multi(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(seq_lens),
                                         _ptr(block_table), max_pages, page_size, B, Hq, Hkv, q_len, D,
@@ -374,3 +462,27 @@ def attn_decode_splitk_multi(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, 
                                         _TORCH_DT[q.dtype], _stream(q.device))
     _check("attn_decode_splitk_multi", rc)
     return out, lse
+
+
+# ---- measurement kernels (include/gqa_ceilings.h) ----------------------------
+
+def ceiling_mfma(n_workgroups: int, iters: int, out: Optional[torch.Tensor] = None) -> Tuple[int, torch.Tensor]:
+    """Launch the MFMA-only loop on the current stream; returns (flops of the
+    launch, its output buffer)."""
+    dev = torch.device("cuda", torch.cuda.current_device())
+    out = _out_tensor("out", out, (n_workgroups * 512,), torch.float32, dev)
+    rc = lib().gqa_ceiling_mfma(int(n_workgroups), int(iters), _ptr(out), _stream(dev))
+    if rc:
+        raise RuntimeError(f"gqa_ceiling_mfma failed ({rc})")
+    return int(lib().gqa_ceiling_mfma_flops(int(n_workgroups), int(iters))), out
+
+
+def ceiling_stream_read(src: torch.Tensor, n_workgroups: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Read every byte of `src` (a contiguous GPU tensor) once on the current stream."""
+    _gpu_contig("src", src)
+    out = _out_tensor("out", out, (n_workgroups,), torch.int32, src.device)
+    rc = lib().gqa_ceiling_stream_read(_ptr(src), src.numel() * src.element_size(), int(n_workgroups), _ptr(out),
+                                       _stream(src.device))
+    if rc:
+        raise RuntimeError(f"gqa_ceiling_stream_read failed ({rc})")
+    return out

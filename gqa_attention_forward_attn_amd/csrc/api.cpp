@@ -2,11 +2,10 @@
 // validation (before any HIP call), instantiation choice and launch on the
 // caller's stream.  No allocation, no synchronisation, no global state.
 #include "gqa_attn.h"
+#include "gqa_attn_test.h"
 
 #include <cmath>
 #include <cstdint>
-#include <cstdlib>
-#include <cstring>
 
 #include <hip/hip_runtime.h>
 
@@ -30,23 +29,26 @@ int to_kernel_dtype(gqa_dtype_t t) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// bf16 / fp16 prefill kernel.  By default the library picks by shape; the
-// environment variable GQA_ATTN_PREFILL_KERNEL=pingpong|fourwave forces one
-// (read at every call, for tests that cover both kernels on the same shapes).
-gqa::PrefillKernel prefill_kernel_choice() {
-    const char* v = std::getenv("GQA_ATTN_PREFILL_KERNEL");
-    if (v && std::strcmp(v, "pingpong") == 0) return gqa::PrefillKernel::kPingPong;
-    if (v && std::strcmp(v, "fourwave") == 0) return gqa::PrefillKernel::kFourWave;
-    return gqa::PrefillKernel::kAuto;
+// Kernel choice of the two bf16 / fp16 prefill kernels: 0 = by shape, 1 =
+// ping-pong, 2 = four-wave (the *_with_kernel entry points of gqa_attn_test.h).
+bool to_prefill_kernel(int kernel, gqa::PrefillKernel* out) {
+    switch (kernel) {
+    case 0: *out = gqa::PrefillKernel::kAuto; return true;
+    case 1: *out = gqa::PrefillKernel::kPingPong; return true;
+    case 2: *out = gqa::PrefillKernel::kFourWave; return true;
+    default: return false;
+    }
 }
 
 }  // namespace
 
 extern "C" {
 
-gqa_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                      int B, int Hq, int Hkv, int q_len, int kv_len, int D,
-                      float scale, int causal, gqa_dtype_t dtype, void* hip_stream) {
+gqa_status_t attn_fwd_with_kernel(const void* q, const void* k, const void* v, void* o, float* lse,
+                                  int B, int Hq, int Hkv, int q_len, int kv_len, int D,
+                                  float scale, int causal, gqa_dtype_t dtype, int kernel, void* hip_stream) {
+    gqa::PrefillKernel choice;
+    if (!to_prefill_kernel(kernel, &choice)) return GQA_ERR_INVALID_ARG;
     if (B < 0 || q_len < 0 || kv_len < 0 || Hq <= 0 || Hkv <= 0 || D <= 0) return GQA_ERR_INVALID_ARG;
     if (Hq % Hkv != 0) return GQA_ERR_INVALID_ARG;
     if (!valid_dtype(dtype)) return GQA_ERR_INVALID_ARG;
@@ -69,9 +71,16 @@ gqa_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, floa
     a.group = Hq / Hkv;
     a.delta = kv_len - q_len;
     a.c = scale * kLog2e;
-    hipError_t e = gqa::launch_prefill(a, D, causal != 0, to_kernel_dtype(dtype), prefill_kernel_choice(),
+    hipError_t e = gqa::launch_prefill(a, D, causal != 0, to_kernel_dtype(dtype), choice,
                                        static_cast<hipStream_t>(hip_stream));
     return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+gqa_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int Hq, int Hkv, int q_len, int kv_len, int D,
+                      float scale, int causal, gqa_dtype_t dtype, void* hip_stream) {
+    return attn_fwd_with_kernel(q, k, v, o, lse, B, Hq, Hkv, q_len, kv_len, D, scale, causal, dtype, 0,
+                                hip_stream);
 }
 
 int attn_fwd_kv_splits(int B, int Hq, int Hkv, int q_len, int kv_len, int D, int causal, gqa_dtype_t dtype) {
@@ -138,10 +147,13 @@ gqa_status_t attn_fwd_split(const void* q, const void* k, const void* v, void* o
     return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 
-gqa_status_t attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
-                                const int* qo_indptr, const int* kv_indptr, const int* kv_indices,
-                                const int* kv_last_page_len, int B, int Hq, int Hkv, int D, int page_size,
-                                int max_q_len, float scale, int causal, gqa_dtype_t dtype, void* hip_stream) {
+gqa_status_t attn_prefill_paged_with_kernel(const void* q, const void* k_cache, const void* v_cache, void* o,
+                                            float* lse, const int* qo_indptr, const int* kv_indptr,
+                                            const int* kv_indices, const int* kv_last_page_len, int B, int Hq,
+                                            int Hkv, int D, int page_size, int max_q_len, float scale, int causal,
+                                            gqa_dtype_t dtype, int kernel, void* hip_stream) {
+    gqa::PrefillKernel choice;
+    if (!to_prefill_kernel(kernel, &choice)) return GQA_ERR_INVALID_ARG;
     if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || max_q_len < 0) return GQA_ERR_INVALID_ARG;
     if (Hq % Hkv != 0) return GQA_ERR_INVALID_ARG;
     if (page_size <= 0 || (page_size & (page_size - 1)) != 0) return GQA_ERR_INVALID_ARG;
@@ -168,9 +180,18 @@ gqa_status_t attn_prefill_paged(const void* q, const void* k_cache, const void* 
     a.kv_indices = kv_indices;
     a.kv_last_page_len = kv_last_page_len;
     a.page_shift = page_shift;
-    hipError_t e = gqa::launch_prefill_paged(a, D, causal != 0, to_kernel_dtype(dtype), prefill_kernel_choice(),
+    hipError_t e = gqa::launch_prefill_paged(a, D, causal != 0, to_kernel_dtype(dtype), choice,
                                              static_cast<hipStream_t>(hip_stream));
     return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+gqa_status_t attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                                const int* qo_indptr, const int* kv_indptr, const int* kv_indices,
+                                const int* kv_last_page_len, int B, int Hq, int Hkv, int D, int page_size,
+                                int max_q_len, float scale, int causal, gqa_dtype_t dtype, void* hip_stream) {
+    return attn_prefill_paged_with_kernel(q, k_cache, v_cache, o, lse, qo_indptr, kv_indptr, kv_indices,
+                                          kv_last_page_len, B, Hq, Hkv, D, page_size, max_q_len, scale, causal,
+                                          dtype, 0, hip_stream);
 }
 
 size_t attn_decode_workspace_bytes_multi(int B, int Hq, int q_len, int D, int n_splits) {

@@ -47,7 +47,9 @@ __device__ __forceinline__ f32x16 mfma_32x32x2(float a, float b, f32x16 c) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Value of x held by lane (l ^ 32), for every lane l.
+// Value of x held by lane (l ^ 32), for every lane l.  The result must be
+// selected per lane: the compiler treats the two results of a swap of one
+// value with itself as equal and folds expressions that use both.
 __device__ __forceinline__ float xor32(float x) {
     uint32_t u = __builtin_bit_cast(uint32_t, x);
     auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
@@ -56,18 +58,6 @@ __device__ __forceinline__ float xor32(float x) {
     uint32_t lane = __lane_id();
     return __builtin_bit_cast(float, lane < 32 ? r[1] : r[0]);
 }
-
-// DPP lane moves inside rows of 16 lanes.  quad_perm / row_half_mirror /
-// row_mirror controls; bound_ctrl makes lanes without a source read 0.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-        0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
-}
-constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
-constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
-constexpr int kRowHalfMirror = 0x141;
-constexpr int kRowMirror = 0x140;
 
 // Lane (l ^ mask) via the LDS crossbar (any mask).
 __device__ __forceinline__ float shfl_xor(float x, int mask) {
@@ -86,7 +76,6 @@ __device__ __forceinline__ uint32_t pack2(f16_tag, float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// Packed pair in the storage type -> two fp32 values.
 // One output row from the 32x32 MFMA accumulator with the queries as columns:
 // lane (q, half) holds dims 32 dt + 8 j + 4 half + 0..3 (j = 0..3) of row q.
 // A lane swap between the two 32-lane halves leaves each lane 16 consecutive
@@ -136,23 +125,6 @@ __device__ __forceinline__ void store_acc_row(TAG, const f32x16 (&acc)[DT], floa
             *reinterpret_cast<u32x4*>(dst + 8) = chunk[2 * dt + 1];
         }
     }
-}
-
-__device__ __forceinline__ float lo_to_f32(bf16_tag, uint32_t u) { return __builtin_bit_cast(float, u << 16); }
-__device__ __forceinline__ float hi_to_f32(bf16_tag, uint32_t u) { return __builtin_bit_cast(float, u & 0xffff0000u); }
-__device__ __forceinline__ float lo_to_f32(f16_tag, uint32_t u) {
-    return (float)__builtin_bit_cast(f16x2, u)[0];
-}
-__device__ __forceinline__ float hi_to_f32(f16_tag, uint32_t u) {
-    return (float)__builtin_bit_cast(f16x2, u)[1];
-}
-
-// fp32 accumulate of a 2-element dot product in the storage type.
-__device__ __forceinline__ float dot2(bf16_tag, uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
-}
-__device__ __forceinline__ float dot2(f16_tag, uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
 }
 
 // Select 16-bit halves of two dwords: lo16(a) | lo16(b) << 16, and hi16(a) | hi16(b) << 16.

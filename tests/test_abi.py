@@ -11,6 +11,8 @@ import gqa_attention_forward_attn_amd as gqa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gqa_attn.h")
+TEST_HEADER = os.path.join(ROOT, "include", "gqa_attn_test.h")
+CEILING_HEADER = os.path.join(ROOT, "include", "gqa_ceilings.h")
 
 OK, INVALID, UNSUPPORTED, WORKSPACE, HIP = 0, 1, 2, 3, 4
 BF16, F16, F32 = gqa.GQA_BF16, gqa.GQA_F16, gqa.GQA_F32
@@ -19,8 +21,8 @@ BF16, F16, F32 = gqa.GQA_BF16, gqa.GQA_F16, gqa.GQA_F32
 P = [ctypes.c_void_p(0x10000 * (i + 1)) for i in range(8)]
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(path=HEADER):
+    text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"if", "sizeof"})
 
@@ -37,6 +39,31 @@ def test_exports_every_declared_symbol(L):
     assert set(names) == set(gqa.EXPORTS)
     for n in names:
         assert hasattr(L, n), f"{n} declared in gqa_attn.h but not exported"
+    test_names = declared_functions(TEST_HEADER)
+    assert set(test_names) == set(gqa.TEST_EXPORTS)
+    for n in test_names:
+        assert hasattr(L, n), f"{n} declared in gqa_attn_test.h but not exported"
+    ceiling_names = declared_functions(CEILING_HEADER)
+    assert set(ceiling_names) == set(gqa.CEILING_EXPORTS)
+    for n in ceiling_names:
+        assert hasattr(L, n), f"{n} declared in gqa_ceilings.h but not exported"
+
+
+def test_ceiling_validation(L):
+    assert L.gqa_ceiling_mfma_flops(256, 100) == 256 * 8 * 100 * 16 * 32768
+    assert L.gqa_ceiling_mfma_flops(0, 100) == 0
+    assert L.gqa_ceiling_mfma(0, 10, P[0], None) == 1
+    assert L.gqa_ceiling_mfma(4, 10, None, None) == 1
+    assert L.gqa_ceiling_stream_read(P[0], 24, 4, P[1], None) == 1    # not a multiple of 16
+    assert L.gqa_ceiling_stream_read(ctypes.c_void_p(0x10008), 64, 4, P[1], None) == 1   # misaligned
+
+
+def test_kernel_choice_validation(L):
+    # the test entry points reject an unknown kernel code before anything else
+    args = (P[0], P[1], P[2], P[3], P[4], 1, 4, 2, 8, 8, 64, 0.125, 1, BF16)
+    assert L.attn_fwd_with_kernel(*args, 3, None) == INVALID
+    assert L.attn_fwd_with_kernel(*args, -1, None) == INVALID
+    assert L.attn_fwd_with_kernel(P[0], P[1], P[2], P[3], P[4], 0, 4, 2, 8, 8, 64, 0.125, 1, BF16, 2, None) == OK
 
 
 def test_status_strings(L):

@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 
 # every block table and CSR pointer set a test passes is also checked on the
 # host before the launch (the kernels themselves trust them)
-os.environ["GQA_ATTN_CHECK_TABLES"] = "1"
+gqa.set_check_tables(True)
 
 TOL = {"f32": (1e-5, 1e-5), "bf16": (2e-2, 1e-3), "f16": (2e-2, 1e-3)}
 DTNAME = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16"}
@@ -41,11 +41,12 @@ def check(o_gpu, lse_gpu, o_ref, lse_ref, dtname, what=""):
     return err_o, err_l
 
 
-def gpu_fwd(q, k, v, causal, scale, canary=True, kv_splits=1):
+def gpu_fwd(q, k, v, causal, scale, canary=True, kv_splits=1, kernel=None):
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     out = torch.full_like(qd, float("nan")) if canary else None
     lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device="cuda") if canary else None
-    o, l = gqa.attn_fwd(qd, kd, vd, causal=causal, scale=scale, out=out, lse=lse, kv_splits=kv_splits)
+    o, l = gqa.attn_fwd(qd, kd, vd, causal=causal, scale=scale, out=out, lse=lse, kv_splits=kv_splits,
+                        kernel=kernel)
     torch.cuda.synchronize()
     return o, l
 
@@ -75,13 +76,12 @@ SMALL_CASES = [(s, kern) for s in SMALL for kern in (PREFILL_KERNELS if s[6] != 
 
 
 @pytest.mark.parametrize("shape,kernel", SMALL_CASES, ids=lambda c: "-".join(map(str, c)) if isinstance(c, tuple) else c)
-def test_prefill_all_elements(shape, kernel, monkeypatch):
-    monkeypatch.setenv("GQA_ATTN_PREFILL_KERNEL", kernel)
+def test_prefill_all_elements(shape, kernel):
     B, Hq, Hkv, Lq, Lk, D, dt, causal = shape
     print(f"prefill case {shape} kernel {kernel}", flush=True)
     q, k, v = W.make_prefill(B, Hq, Hkv, Lq, Lk, D, dt, seed=sum(shape[:6]))
     scale = W.fp32_scale(D)
-    o, l = gpu_fwd(q, k, v, causal, scale)
+    o, l = gpu_fwd(q, k, v, causal, scale, kernel=kernel)
     o_ref, l_ref = oracle.attn_fwd(q, k, v, scale, causal)
     check(o.double().cpu().numpy(), l.double().cpu().numpy(), o_ref, l_ref, dt, str(shape))
 
@@ -102,7 +102,7 @@ SPLIT = [
 
 
 @pytest.mark.parametrize("case", SPLIT, ids=lambda c: "-".join(map(str, c)))
-def test_prefill_split_all_elements(case, monkeypatch):
+def test_prefill_split_all_elements(case):
     B, Hq, Hkv, Lq, Lk, D, dt, causal, S = case
     print(f"split prefill case {case}", flush=True)
     q, k, v = W.make_prefill(B, Hq, Hkv, Lq, Lk, D, dt, seed=sum(case[:6]) + S)
@@ -113,8 +113,7 @@ def test_prefill_split_all_elements(case, monkeypatch):
     # the merge of the ranges equals the single pass of the same kernel up to
     # rounding: the tiles and their rounded weights are the same, only the
     # order of the fp32 sums and the final rounding differ
-    monkeypatch.setenv("GQA_ATTN_PREFILL_KERNEL", "pingpong")
-    o1, l1 = gpu_fwd(q, k, v, causal, scale, kv_splits=1)
+    o1, l1 = gpu_fwd(q, k, v, causal, scale, kv_splits=1, kernel="pingpong")
     lf, l1f = l.cpu(), l1.cpu()
     assert torch.equal(torch.isneginf(lf), torch.isneginf(l1f))
     fin = torch.isfinite(l1f)
@@ -134,7 +133,7 @@ RECOMMENDED_SPLIT = [
 
 
 @pytest.mark.parametrize("shape", RECOMMENDED_SPLIT, ids=lambda c: "-".join(map(str, c)))
-def test_prefill_recommended_split_small_grid(shape, monkeypatch):
+def test_prefill_recommended_split_small_grid(shape):
     B, Hq, Hkv, Lq, Lk = shape
     S = gqa.lib().attn_fwd_kv_splits(B, Hq, Hkv, Lq, Lk, 128, 1, gqa._TORCH_DT[torch.bfloat16])
     print(f"recommended split {shape}: {S} ranges", flush=True)
@@ -142,12 +141,9 @@ def test_prefill_recommended_split_small_grid(shape, monkeypatch):
     q, k, v = W.make_prefill(B, Hq, Hkv, Lq, Lk, 128, "bf16", seed=Lq + Lk + Hq)
     scale = W.fp32_scale(128)
     o, l = gpu_fwd(q, k, v, True, scale, kv_splits=None)
-    rows = sample_rows(B, Hq, Lq, 512, Lq + Hq)
-    o_ref, l_ref = oracle.attn_fwd(q, k, v, scale, True, rows=rows)
-    check(o.double().cpu().numpy().reshape(-1, 128)[rows], l.double().cpu().numpy().reshape(-1)[rows],
-          o_ref, l_ref, "bf16", str(shape))
-    monkeypatch.setenv("GQA_ATTN_PREFILL_KERNEL", "pingpong")
-    o1, l1 = gpu_fwd(q, k, v, True, scale, kv_splits=1)
+    o_ref, l_ref = oracle.attn_fwd(q, k, v, scale, True)
+    check(o.double().cpu().numpy(), l.double().cpu().numpy(), o_ref, l_ref, "bf16", str(shape))
+    o1, l1 = gpu_fwd(q, k, v, True, scale, kv_splits=1, kernel="pingpong")
     assert float((l.cpu() - l1.cpu()).abs().max()) <= 1e-5
     assert float((o.float() - o1.float()).abs().max()) <= 1.6e-2
 
@@ -158,21 +154,19 @@ def test_prefill_kv_len_zero():
     assert torch.all(o.float() == 0) and torch.all(torch.isneginf(l))
 
 
-# ---- prefill at the workload sizes: sampled rows ---------------------------
+# ---- prefill at the workload sizes: every element ----------------------------
+# The oracle runs once per workload (cached for the module) and every kernel
+# variant is compared with it on all rows of O and LSE.
 
-def sample_rows(B, Hq, Lq, n_random, seed):
-    """Rows that always include the first/last positions and tile edges of every
-    head, plus random positions."""
-    g = np.random.default_rng(seed)
-    pos = {0, 1, 31, 32, 63, 64, 127, 128, Lq // 2, Lq - 2, Lq - 1}
-    pos = sorted(p for p in pos if 0 <= p < Lq)
-    rows = []
-    for b in range(B):
-        for h in range(Hq):
-            base = (b * Hq + h) * Lq
-            rows.extend(base + p for p in pos)
-    rows.extend(g.integers(0, B * Hq * Lq, size=n_random).tolist())
-    return np.unique(np.array(rows, dtype=np.int64))
+_WORKLOAD_ORACLE = {}
+
+
+def workload_oracle(spec):
+    if spec.name not in _WORKLOAD_ORACLE:
+        q, k, v = W.make_prefill_spec(spec)
+        scale = W.fp32_scale(spec.D)
+        _WORKLOAD_ORACLE[spec.name] = (q, k, v, scale, oracle.attn_fwd(q, k, v, scale, spec.causal))
+    return _WORKLOAD_ORACLE[spec.name]
 
 
 WORKLOAD_CASES = [(s, kern) for s in W.PREFILL_WORKLOADS
@@ -181,27 +175,19 @@ WORKLOAD_CASES = [(s, kern) for s in W.PREFILL_WORKLOADS
 
 @pytest.mark.parametrize("spec,kernel", WORKLOAD_CASES,
                          ids=lambda c: c.name if hasattr(c, "name") else c)
-def test_prefill_workload_sampled(spec, kernel, monkeypatch):
+def test_prefill_workload_all_elements(spec, kernel):
     # "split": key ranges merged by LSE, with the library's range count for the
     # shape (at least 2, so that every workload also runs the split path)
     splits = 1
     if kernel == "split":
         splits = max(2, gqa.lib().attn_fwd_kv_splits(spec.B, spec.Hq, spec.Hkv, spec.q_len, spec.kv_len,
                                                      spec.D, int(spec.causal), gqa._TORCH_DT[W._DTYPES[spec.dtype]]))
-    else:
-        monkeypatch.setenv("GQA_ATTN_PREFILL_KERNEL", kernel)
     print(f"workload {spec.name} kernel {kernel} kv_splits {splits}", flush=True)
-    q, k, v = W.make_prefill_spec(spec)
-    scale = W.fp32_scale(spec.D)
-    o, l = gpu_fwd(q, k, v, spec.causal, scale, kv_splits=splits)
-    o = o.double().cpu().numpy().reshape(-1, spec.D)
-    l = l.double().cpu().numpy().reshape(-1)
-    # properties at every row: finite (every row here sees at least one key)
-    assert np.isfinite(o).all() and np.isfinite(l).all()
-    rows = sample_rows(spec.B, spec.Hq, spec.q_len, 1024, spec.seed)
-    o_ref, l_ref = oracle.attn_fwd(q, k, v, scale, spec.causal, rows=rows)
-    e_o, e_l = check(o[rows], l[rows], o_ref, l_ref, spec.dtype, spec.name)
-    print(f"{spec.name}: rows={len(rows)} max|dO|={e_o:.3e} max|dLSE|={e_l:.3e}")
+    q, k, v, scale, (o_ref, l_ref) = workload_oracle(spec)
+    o, l = gpu_fwd(q, k, v, spec.causal, scale, kv_splits=splits,
+                   kernel=kernel if kernel in PREFILL_KERNELS else None)
+    e_o, e_l = check(o.double().cpu().numpy(), l.double().cpu().numpy(), o_ref, l_ref, spec.dtype, spec.name)
+    print(f"{spec.name} ({kernel}): all {l_ref.size} rows, max|dO|={e_o:.3e} max|dLSE|={e_l:.3e}")
 
 
 def test_causal_row_zero_exact():
@@ -452,14 +438,14 @@ def test_decode_multi_dense_matches_paged():
 
 # ---- ragged prefill over a paged cache ------------------------------------------
 
-def gpu_prefill_paged(inp, causal, scale, last=True):
+def gpu_prefill_paged(inp, causal, scale, last=True, kernel=None):
     q = inp.q.cuda()
     out = torch.full_like(q, float("nan"))
     lse = torch.full(q.shape[:2], float("nan"), dtype=torch.float32, device="cuda")
     o, l = gqa.attn_prefill_paged(q, inp.k_cache.cuda(), inp.v_cache.cuda(), inp.qo_indptr.cuda(),
                                   inp.kv_indptr.cuda(), inp.kv_indices.cuda(), inp.max_q_len,
                                   kv_last_page_len=inp.kv_last_page_len.cuda() if last else None,
-                                  causal=causal, scale=scale, out=out, lse=lse)
+                                  causal=causal, scale=scale, out=out, lse=lse, kernel=kernel)
     torch.cuda.synchronize()
     return o.double().cpu().numpy(), l.double().cpu().numpy()
 
@@ -487,8 +473,7 @@ PAGED_PREFILL = [
 # both kernels have a paged mode (chosen by the grid size; forced here)
 @pytest.mark.parametrize("kernel", PREFILL_KERNELS)
 @pytest.mark.parametrize("case", PAGED_PREFILL, ids=lambda c: "-".join(map(str, c[:6])))
-def test_prefill_paged_cases(case, kernel, monkeypatch):
-    monkeypatch.setenv("GQA_ATTN_PREFILL_KERNEL", kernel)
+def test_prefill_paged_cases(case, kernel):
     Hq, Hkv, D, dt, ps, causal, lens = case
     print(f"paged prefill case {case[:6]} kernel {kernel}", flush=True)
     if isinstance(lens[0], list):
@@ -499,60 +484,53 @@ def test_prefill_paged_cases(case, kernel, monkeypatch):
         inp = W.make_paged_prefill(B, Hq, Hkv, D, dt, seed=Hq + D + ps, q_lo=qlo, q_hi=qhi,
                                    prefix_lo=plo, prefix_hi=phi, page_size=ps)
     scale = W.fp32_scale(D)
-    o, l = gpu_prefill_paged(inp, causal, scale)
+    o, l = gpu_prefill_paged(inp, causal, scale, kernel=kernel)
     o_ref, l_ref = oracle_prefill_paged(inp, causal, scale)
     check(o, l, o_ref, l_ref, dt, str(case[:6]))
 
 
 @pytest.mark.parametrize("kernel", PREFILL_KERNELS)
-def test_prefill_paged_full_pages_without_last_len(kernel, monkeypatch):
+def test_prefill_paged_full_pages_without_last_len(kernel):
     # kv_last_page_len omitted: every page is full
-    monkeypatch.setenv("GQA_ATTN_PREFILL_KERNEL", kernel)
     inp = W.make_paged_prefill(3, 8, 2, 64, "bf16", seed=50, page_size=32, q_lens=[40, 64, 3],
                                kv_lens=[64, 96, 32])
-    o, l = gpu_prefill_paged(inp, True, 0.125, last=False)
+    o, l = gpu_prefill_paged(inp, True, 0.125, last=False, kernel=kernel)
     o_ref, l_ref = oracle_prefill_paged(inp, True, 0.125, last=False)
     check(o, l, o_ref, l_ref, "bf16", "full pages")
 
 
 @pytest.mark.parametrize("kernel", PREFILL_KERNELS)
-def test_prefill_paged_equals_dense_forward(kernel, monkeypatch):
+def test_prefill_paged_equals_dense_forward(kernel):
     # one request over an identity page table is the dense forward of the same
     # K/V on the same kernel
-    monkeypatch.setenv("GQA_ATTN_PREFILL_KERNEL", kernel)
     inp = W.make_paged_prefill(1, 8, 2, 128, "bf16", seed=51, page_size=64, q_lens=[300], kv_lens=[700],
                                permute=False)
-    o1, l1 = gpu_prefill_paged(inp, True, 0.088)
+    o1, l1 = gpu_prefill_paged(inp, True, 0.088, kernel=kernel)
     kd = inp.k_cache.reshape(-1, 2, 128)[:700].permute(1, 0, 2).unsqueeze(0).contiguous()
     vd = inp.v_cache.reshape(-1, 2, 128)[:700].permute(1, 0, 2).unsqueeze(0).contiguous()
     qd = inp.q.permute(1, 0, 2).unsqueeze(0).contiguous()
-    o2, l2 = gpu_fwd(qd, kd, vd, True, 0.088)
+    o2, l2 = gpu_fwd(qd, kd, vd, True, 0.088, kernel=kernel)
     o2 = o2.double().cpu().numpy()[0].transpose(1, 0, 2)
     l2 = l2.double().cpu().numpy()[0].T
     # the same kernel arithmetic on the same keys: bitwise equal
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
+_RAGGED_ORACLE = {}
+
+
 @pytest.mark.parametrize("kernel", PREFILL_KERNELS)
-def test_prefill_paged_workload_sampled(kernel, monkeypatch):
-    monkeypatch.setenv("GQA_ATTN_PREFILL_KERNEL", kernel)
+def test_prefill_paged_workload_all_elements(kernel):
     spec = W.RAGGED_PAGED_PREFILL
-    print("workload ragged_paged_prefill", flush=True)
-    inp = W.make_paged_prefill_spec(spec)
-    scale = W.fp32_scale(spec.D)
-    o, l = gpu_prefill_paged(inp, spec.causal, scale)
-    total = o.shape[0] * spec.Hq
-    g = np.random.default_rng(7)
-    rows = []
-    for b in range(spec.B):  # first and last token of every request, all heads
-        t0, t1 = int(inp.qo_indptr[b]), int(inp.qo_indptr[b + 1])
-        for t in {t0, t1 - 1}:
-            rows.extend(range(t * spec.Hq, (t + 1) * spec.Hq))
-    rows = np.unique(np.concatenate([np.asarray(rows), g.choice(total, 1024, replace=False)]))
-    o_ref, l_ref = oracle_prefill_paged(inp, spec.causal, scale, rows=rows)
-    e_o, e_l = check(o.reshape(-1, spec.D)[rows], l.reshape(-1)[rows], o_ref, l_ref, "bf16",
-                     "ragged_paged_prefill")
-    print(f"ragged_paged_prefill: {len(rows)} rows, max|dO|={e_o:.3e} max|dLSE|={e_l:.3e}")
+    print(f"workload ragged_paged_prefill kernel {kernel}", flush=True)
+    if "ref" not in _RAGGED_ORACLE:
+        inp = W.make_paged_prefill_spec(spec)
+        scale = W.fp32_scale(spec.D)
+        _RAGGED_ORACLE["ref"] = (inp, scale, oracle_prefill_paged(inp, spec.causal, scale))
+    inp, scale, (o_ref, l_ref) = _RAGGED_ORACLE["ref"]
+    o, l = gpu_prefill_paged(inp, spec.causal, scale, kernel=kernel)
+    e_o, e_l = check(o, l, o_ref, l_ref, "bf16", "ragged_paged_prefill")
+    print(f"ragged_paged_prefill ({kernel}): all {l_ref.size} rows, max|dO|={e_o:.3e} max|dLSE|={e_l:.3e}")
 
 
 # ---- decode over an 8-bit E4M3 cache ----------------------------------------------
@@ -697,13 +675,12 @@ def _last_batch(shape, data):
 
 
 @pytest.mark.parametrize("kernel", PREFILL_KERNELS + ["split", "f32"])
-def test_prefill_kv_past_2g_elements(kernel, monkeypatch):
+def test_prefill_kv_past_2g_elements(kernel):
     # 129 sequences of 65536 keys: the last sequence's K and V start at element 2^31
     dt = "f32" if kernel == "f32" else "bf16"
     B, Hq, Hkv, ql, kl, D = (129, 2, 2, 64, 65536, 128) if dt == "f32" else (129, 8, 2, 64, 65536, 128)
     assert (B - 1) * Hkv * kl * D == BIG
-    if kernel in PREFILL_KERNELS:
-        monkeypatch.setenv("GQA_ATTN_PREFILL_KERNEL", kernel)
+    kern = kernel if kernel in PREFILL_KERNELS else None
     splits = 2 if kernel == "split" else 1
     print(f"prefill K/V past 2^31 elements, kernel {kernel}", flush=True)
     q1, k1, v1 = W.make_prefill(1, Hq, Hkv, ql, kl, D, dt, seed=131)
@@ -711,41 +688,38 @@ def test_prefill_kv_past_2g_elements(kernel, monkeypatch):
     q = _last_batch((B, Hq, ql, D), q1)
     k = _last_batch((B, Hkv, kl, D), k1)
     v = _last_batch((B, Hkv, kl, D), v1)
-    o, l = gqa.attn_fwd(q, k, v, causal=True, scale=scale, kv_splits=splits)
+    o, l = gqa.attn_fwd(q, k, v, causal=True, scale=scale, kv_splits=splits, kernel=kern)
     o_big, l_big = o[B - 1:].cpu(), l[B - 1:].cpu()
     del q, k, v, o, l
     _release()
-    o_small, l_small = gqa.attn_fwd(q1.cuda(), k1.cuda(), v1.cuda(), causal=True, scale=scale, kv_splits=splits)
+    o_small, l_small = gqa.attn_fwd(q1.cuda(), k1.cuda(), v1.cuda(), causal=True, scale=scale, kv_splits=splits,
+                                    kernel=kern)
     assert torch.equal(o_big, o_small.cpu()) and torch.equal(l_big, l_small.cpu())
-    rows = sample_rows(1, Hq, ql, 64, 131)
-    o_ref, l_ref = oracle.attn_fwd(q1, k1, v1, scale, True, rows=rows)
-    check(o_big.double().numpy().reshape(-1, D)[rows], l_big.double().numpy().reshape(-1)[rows],
-          o_ref, l_ref, dt, f"K/V past 2^31, {kernel}")
+    o_ref, l_ref = oracle.attn_fwd(q1, k1, v1, scale, True)
+    check(o_big.double().numpy(), l_big.double().numpy(), o_ref, l_ref, dt, f"K/V past 2^31, {kernel}")
 
 
 @pytest.mark.parametrize("kernel", PREFILL_KERNELS)
-def test_prefill_qo_past_2g_elements(kernel, monkeypatch):
+def test_prefill_qo_past_2g_elements(kernel):
     # 1025 sequences x 8 heads x 2048 positions x 128 dims: the last sequence's
     # Q and O rows start at element 2^31
     B, Hq, Hkv, L, D = 1025, 8, 2, 2048, 128
     assert (B - 1) * Hq * L * D == BIG
-    monkeypatch.setenv("GQA_ATTN_PREFILL_KERNEL", kernel)
     print(f"prefill Q/O past 2^31 elements, kernel {kernel}", flush=True)
     q1, k1, v1 = W.make_prefill(1, Hq, Hkv, L, L, D, "bf16", seed=1025)
     scale = W.fp32_scale(D)
     q = _last_batch((B, Hq, L, D), q1)
     k = _last_batch((B, Hkv, L, D), k1)
     v = _last_batch((B, Hkv, L, D), v1)
-    o, l = gqa.attn_fwd(q, k, v, causal=True, scale=scale, kv_splits=1)
+    o, l = gqa.attn_fwd(q, k, v, causal=True, scale=scale, kv_splits=1, kernel=kernel)
     o_big, l_big = o[B - 1:].cpu(), l[B - 1:].cpu()
     del q, k, v, o, l
     _release()
-    o_small, l_small = gqa.attn_fwd(q1.cuda(), k1.cuda(), v1.cuda(), causal=True, scale=scale, kv_splits=1)
+    o_small, l_small = gqa.attn_fwd(q1.cuda(), k1.cuda(), v1.cuda(), causal=True, scale=scale, kv_splits=1,
+                                    kernel=kernel)
     assert torch.equal(o_big, o_small.cpu()) and torch.equal(l_big, l_small.cpu())
-    rows = sample_rows(1, Hq, L, 128, 1025)
-    o_ref, l_ref = oracle.attn_fwd(q1, k1, v1, scale, True, rows=rows)
-    check(o_big.double().numpy().reshape(-1, D)[rows], l_big.double().numpy().reshape(-1)[rows],
-          o_ref, l_ref, "bf16", f"Q/O past 2^31, {kernel}")
+    o_ref, l_ref = oracle.attn_fwd(q1, k1, v1, scale, True)
+    check(o_big.double().numpy(), l_big.double().numpy(), o_ref, l_ref, "bf16", f"Q/O past 2^31, {kernel}")
 
 
 def test_decode_pages_past_4gib():
@@ -795,11 +769,10 @@ def test_decode_fp8_pages_past_4gib():
 
 
 @pytest.mark.parametrize("kernel", PREFILL_KERNELS)
-def test_prefill_paged_pages_past_4gib(kernel, monkeypatch):
+def test_prefill_paged_pages_past_4gib(kernel):
     # paged prefill over 256-token pages of 8 heads x 128 dims: every page of
     # the batch at or above page 8192 (element 2^31)
     Hq, Hkv, D, ps, first = 32, 8, 128, 256, 8192
-    monkeypatch.setenv("GQA_ATTN_PREFILL_KERNEL", kernel)
     print(f"paged prefill pages past 4 GiB, kernel {kernel}", flush=True)
     inp = W.make_paged_prefill(3, Hq, Hkv, D, "bf16", seed=8192, q_lo=1, q_hi=300, prefix_lo=0, prefix_hi=700,
                                page_size=ps)
@@ -807,10 +780,10 @@ def test_prefill_paged_pages_past_4gib(kernel, monkeypatch):
     big = W.PagedPrefillInputs(inp.q, _pool(inp.k_cache, first, float("nan")),
                                _pool(inp.v_cache, first, float("nan")), inp.qo_indptr, inp.kv_indptr,
                                _shift_table(inp.kv_indices, first), inp.kv_last_page_len, ps, inp.max_q_len)
-    o_big, l_big = gpu_prefill_paged(big, True, scale)
+    o_big, l_big = gpu_prefill_paged(big, True, scale, kernel=kernel)
     del big
     _release()
-    o_small, l_small = gpu_prefill_paged(inp, True, scale)
+    o_small, l_small = gpu_prefill_paged(inp, True, scale, kernel=kernel)
     assert np.array_equal(o_big, o_small) and np.array_equal(l_big, l_small)
     o_ref, l_ref = oracle_prefill_paged(inp, True, scale)
     check(o_big, l_big, o_ref, l_ref, "bf16", f"paged prefill past 4 GiB, {kernel}")
