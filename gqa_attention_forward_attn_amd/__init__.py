@@ -26,7 +26,8 @@ _TORCH_DT = {torch.float32: GQA_F32, torch.float16: GQA_F16, torch.bfloat16: GQA
 EXPORTS = ("attn_fwd", "attn_fwd_split", "attn_fwd_split_workspace_bytes", "attn_fwd_kv_splits",
            "attn_prefill_paged", "attn_decode_workspace_bytes", "attn_decode_splitk",
            "attn_decode_splitk_fp8",
-           "attn_decode_workspace_bytes_multi", "attn_decode_splitk_multi", "attn_status_str")
+           "attn_decode_workspace_bytes_multi", "attn_decode_splitk_multi", "attn_decode_splitk_noalloc",
+           "attn_status_str")
 # Every symbol include/gqa_attn_test.h declares (kernel selection for tests).
 TEST_EXPORTS = ("attn_fwd_with_kernel", "attn_prefill_paged_with_kernel")
 # Every symbol include/gqa_ceilings.h declares (measurement kernels).
@@ -74,6 +75,9 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_splitk.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                      f32, i32, vp, sz, i32, vp]
     L.attn_decode_splitk.restype = i32
+    L.attn_decode_splitk_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                             f32, i32, i32, vp]
+    L.attn_decode_splitk_noalloc.restype = i32
     L.attn_decode_workspace_bytes_multi.argtypes = [i32, i32, i32, i32, i32]
     L.attn_decode_workspace_bytes_multi.restype = sz
     L.attn_decode_splitk_multi.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
@@ -393,6 +397,31 @@ def attn_decode_splitk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_le
                                   workspace.numel() * workspace.element_size(),
                                   _TORCH_DT[q.dtype], _stream(q.device))
     _check("attn_decode_splitk", rc)
+    return out, lse
+
+
+def attn_decode_splitk_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens: torch.Tensor,
+                               out: torch.Tensor, lse: torch.Tensor, block_table: Optional[torch.Tensor] = None,
+                               n_splits: int = 16, scale: Optional[float] = None,
+                               max_kv_len: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """attn_decode_splitk with the library's fixed device scratch instead of a
+    workspace: nothing is allocated, so `out` [B,Hq,D] and `lse` [B,Hq] fp32
+    must be given.  Calls that overlap on one GPU race on the scratch."""
+    if q.dim() != 3:
+        raise ValueError("q must be [B, Hq, D]")
+    B, Hq, D = q.shape
+    Hkv, page_size, max_pages, max_kv_len = _decode_geometry(q, k, v, seq_lens, block_table, max_kv_len, q.dtype)
+    if check_tables:
+        check_decode_tables(seq_lens, block_table, page_size, k.shape[0], max_kv_len)
+    if out is None or lse is None:
+        raise ValueError("out and lse must be given (this call allocates nothing)")
+    out = _out_tensor("out", out, q.shape, q.dtype, q.device)
+    lse = _out_tensor("lse", lse, (B, Hq), torch.float32, q.device)
+    sc = default_scale(D) if scale is None else float(scale)
+    rc = lib().attn_decode_splitk_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(seq_lens),
+                                          _ptr(block_table), max_pages, page_size, B, Hq, Hkv, D, max_kv_len, sc,
+                                          int(n_splits), _TORCH_DT[q.dtype], _stream(q.device))
+    _check("attn_decode_splitk_noalloc", rc)
     return out, lse
 
 

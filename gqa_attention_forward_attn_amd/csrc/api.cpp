@@ -1,6 +1,8 @@
 // api.cpp - the extern "C" boundary declared in include/gqa_attn.h: argument
 // validation (before any HIP call), instantiation choice and launch on the
-// caller's stream.  No allocation, no synchronisation, no global state.
+// caller's stream.  No allocation, no synchronisation; the only global state
+// is the per-device address of the fixed scratch array that
+// attn_decode_splitk_noalloc uses (csrc/scratch.hip).
 #include "gqa_attn.h"
 #include "gqa_attn_test.h"
 
@@ -306,6 +308,25 @@ gqa_status_t attn_decode_splitk(const void* q, const void* k, const void* v, voi
     return attn_decode_splitk_multi(q, k, v, o, lse, seq_lens, block_table, max_pages_per_seq, page_size,
                                     B, Hq, Hkv, 1, D, max_kv_len, scale, n_splits, workspace,
                                     workspace_bytes, dtype, hip_stream);
+}
+
+gqa_status_t attn_decode_splitk_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                        const int* seq_lens, const int* block_table,
+                                        int max_pages_per_seq, int page_size,
+                                        int B, int Hq, int Hkv, int D, int max_kv_len,
+                                        float scale, int n_splits, gqa_dtype_t dtype, void* hip_stream) {
+    // the sizes first: a request beyond the fixed scratch is refused before
+    // any HIP call; invalid arguments are left to attn_decode_splitk's checks
+    const size_t need = attn_decode_workspace_bytes(B, Hq, D, n_splits);
+    if (need > gqa::scratch_capacity_bytes()) return GQA_ERR_WORKSPACE;
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    if (need > 0) {
+        if (gqa::scratch_device_ptr(&ws) != hipSuccess) return GQA_ERR_HIP;
+        ws_bytes = gqa::scratch_capacity_bytes();
+    }
+    return attn_decode_splitk(q, k, v, o, lse, seq_lens, block_table, max_pages_per_seq, page_size, B, Hq, Hkv,
+                              D, max_kv_len, scale, n_splits, ws, ws_bytes, dtype, hip_stream);
 }
 
 const char* attn_status_str(gqa_status_t s) {

@@ -82,6 +82,11 @@ struct DecodeArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream);
+
+// The library's fixed device scratch (csrc/scratch.hip): its size, and the
+// address of the current device's copy (looked up once per device).
+size_t scratch_capacity_bytes();
+hipError_t scratch_device_ptr(void** out);
 // K/V as E4M3 bytes with scale-shift words (q_len = 1; pages of >= 16 tokens or dense).
 hipError_t launch_decode_fp8(const DecodeArgs& a, int dtype, hipStream_t stream);
 

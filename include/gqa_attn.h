@@ -48,8 +48,10 @@
  *     launched and outputs are untouched.  No exception crosses the ABI.
  *   - Outputs must not alias inputs.
  *   - Tensors are contiguous, row-major, in the layouts given per call.
- *   - The library holds no mutable global state; calls from several host
- *     threads on different streams are safe.
+ *   - The library holds no mutable global state apart from the per-device
+ *     address of the fixed scratch of attn_decode_splitk_noalloc; calls from
+ *     several host threads on different streams are safe, except
+ *     overlapping attn_decode_splitk_noalloc calls on one GPU.
  */
 #ifndef GQA_ATTN_H
 #define GQA_ATTN_H
@@ -309,6 +311,36 @@ gqa_status_t attn_decode_splitk_multi(const void* q, const void* k, const void* 
                                       float scale, int n_splits,
                                       void* workspace, size_t workspace_bytes,
                                       gqa_dtype_t dtype, void* hip_stream);
+
+/*
+ * attn_decode_splitk_noalloc - attn_decode_splitk without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).
+ *
+ * The per-chunk partial outputs and LSEs go to a fixed array of 32 MiB in the
+ * library's device code object instead of a caller workspace: each GPU the
+ * library runs on holds its own copy until the process ends; its address is
+ * looked up once per device (with that device current) on the first call.
+ * The call itself allocates nothing.  Every other argument, layout and result
+ * is that of attn_decode_splitk; the result is bitwise the same.
+ *
+ * Limit: attn_decode_workspace_bytes(B, Hq, D, n_splits) must not exceed
+ * 32 MiB (33554432 bytes: at D = 128 with 32 heads and 16 chunks, up to 127
+ * sequences);
+ * larger requests return GQA_ERR_WORKSPACE before any HIP call.
+ * The array is shared by every call on one GPU and keeps the last call's
+ * contents (nothing in it has to start at zero: each chunk's partial is
+ * written before the merge reads it).  Calls that overlap in time on one GPU
+ * (several streams, or several host threads) race on it and give undefined
+ * results: order them on one stream, or use attn_decode_splitk with a
+ * workspace per stream.  hip_stream must belong to the current device.
+ * Returns GQA_ERR_HIP if the array's address cannot be obtained.
+ */
+gqa_status_t attn_decode_splitk_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                        const int* seq_lens, const int* block_table,
+                                        int max_pages_per_seq, int page_size,
+                                        int B, int Hq, int Hkv, int D, int max_kv_len,
+                                        float scale, int n_splits, gqa_dtype_t dtype, void* hip_stream);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* attn_status_str(gqa_status_t s);

@@ -49,6 +49,14 @@ def test_exports_every_declared_symbol(L):
         assert hasattr(L, n), f"{n} declared in gqa_ceilings.h but not exported"
 
 
+def test_noalloc_decode_rejects_requests_beyond_its_scratch(L):
+    # B * Hq * n_splits * (D + 1) * 4 bytes above the fixed 32 MiB: refused
+    # before any HIP call (so this runs without a GPU)
+    p = [P[i] for i in range(7)]
+    assert L.attn_decode_splitk_noalloc(*p, 4, 256, 1024, 32, 8, 128, 1024, 0.088, 16, BF16, None) == WORKSPACE
+    assert L.attn_decode_splitk_noalloc(*p, 4, 256, 128, 32, 8, 128, 1024, 0.088, 16, BF16, None) == WORKSPACE  # 33.8 MB
+
+
 def test_ceiling_validation(L):
     assert L.gqa_ceiling_mfma_flops(256, 100) == 256 * 8 * 100 * 16 * 32768
     assert L.gqa_ceiling_mfma_flops(0, 100) == 0
