@@ -77,6 +77,16 @@ def _load():
     lib.oracle_attn_decode_fp8.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                            i32, f64, vp, i64, vp, vp]
     lib.oracle_attn_decode_fp8.restype = i32
+    lib.oracle_attn_fwd_bias.argtypes = [vp, vp, vp, i32, vp, i32, i64, i64, i64, i32, i32, i32, i32, i32, i32,
+                                         f64, i32, vp, i64, vp, vp]
+    lib.oracle_attn_fwd_bias.restype = i32
+    lib.oracle_attn_decode_bias.argtypes = [vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                            f64, vp, i32, i64, i64, i64, vp, i64, vp, vp]
+    lib.oracle_attn_decode_bias.restype = i32
+    lib.oracle_splitk_merge.argtypes = [vp, vp, i64, i32, i32, vp, vp]
+    lib.oracle_splitk_merge.restype = i32
+    lib.oracle_splitk_merge_backward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, vp, vp]
+    lib.oracle_splitk_merge_backward.restype = i32
     _lib = lib
     return lib
 
@@ -342,3 +352,105 @@ def attn_decode_fp8(q, k8, v8, k_ss, v_ss, seq_lens, scale: float, block_table=N
     if r is None:
         return o.reshape(B, Hq, D), lse.reshape(B, Hq)
     return o, lse
+
+
+def _full_bias(bias, shape) -> torch.Tensor:
+    """The bias as a contiguous tensor of the full logical shape (broadcast
+    dimensions materialised), in its own storage format."""
+    b = torch.as_tensor(bias).detach().to("cpu")
+    if b.dtype not in _DT:
+        raise TypeError(f"unsupported bias dtype {b.dtype}")
+    return b.expand(*shape).contiguous()
+
+
+def attn_fwd_bias(q, k, v, bias, scale: float, causal: bool, rows=None):
+    """Forward with an additive bias: s_ij = scale * q_i.k_j + bias[b, h, i, j].
+
+    bias: a tensor broadcastable to [B, Hq, q_len, kv_len] (any float storage
+    format; -inf masks a key).  Other arguments and results as attn_fwd.
+    """
+    q, k, v = _cpu(q), _cpu(k), _cpu(v)
+    dt = _dt(q, k, v)
+    B, Hq, q_len, D = q.shape
+    _, Hkv, kv_len, _ = k.shape
+    bf = _full_bias(bias, (B, Hq, q_len, kv_len))
+    r = _rows(rows)
+    n = B * Hq * q_len if r is None else r.shape[0]
+    o = np.empty((n, D), dtype=np.float64)
+    lse = np.empty((n,), dtype=np.float64)
+    rc = _load().oracle_attn_fwd_bias(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(bf), _DT[bf.dtype],
+                                      Hq * q_len * kv_len, q_len * kv_len, kv_len,
+                                      B, Hq, Hkv, q_len, kv_len, D, float(scale), int(bool(causal)),
+                                      _np_ptr(r), n, _np_ptr(o), _np_ptr(lse))
+    if rc:
+        raise ValueError("oracle_attn_fwd_bias: bad arguments")
+    if r is None:
+        return o.reshape(B, Hq, q_len, D), lse.reshape(B, Hq, q_len)
+    return o, lse
+
+
+def attn_decode_bias(q, k, v, seq_lens, bias, scale: float, block_table=None, max_kv_len=None, rows=None):
+    """Decode of q_len queries per sequence (as attn_decode_multi; q [B, Hq,
+    q_len, D]) with an additive bias: query i of sequence b, head h, key t gets
+    bias[b, h, i, t].  bias: broadcastable to [B, Hq, q_len, L] with L >= every
+    sequence length.  Returns (o [B, Hq, q_len, D], lse [B, Hq, q_len]) or, with
+    rows, (o [n, D], lse [n]) for flat ids (b*Hq + h)*q_len + i."""
+    q, k, v, dt, B, Hq, D, sl, bt, max_pages, page_size, Hkv, max_kv_len = _decode_common(
+        q, k, v, seq_lens, block_table, max_kv_len)
+    q_len = q.shape[2]
+    bt_in = torch.as_tensor(bias)
+    L = bt_in.shape[-1]
+    bf = _full_bias(bt_in, (B, Hq, q_len, L))
+    r = _rows(rows)
+    n = B * Hq * q_len if r is None else r.shape[0]
+    o = np.empty((n, D), dtype=np.float64)
+    lse = np.empty((n,), dtype=np.float64)
+    if sl.numel() and int(sl.max()) > L:
+        raise ValueError("the bias has fewer keys than a sequence")
+    rc = _load().oracle_attn_decode_bias(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(sl), _ptr(bt), max_pages,
+                                         page_size, B, Hq, Hkv, q_len, D, max_kv_len, float(scale),
+                                         _ptr(bf), _DT[bf.dtype], Hq * q_len * L, q_len * L, L,
+                                         _np_ptr(r), n, _np_ptr(o), _np_ptr(lse))
+    if rc:
+        raise ValueError("oracle_attn_decode_bias: bad arguments")
+    if r is None:
+        return o.reshape(B, Hq, q_len, D), lse.reshape(B, Hq, q_len)
+    return o, lse
+
+
+def _f64(a) -> np.ndarray:
+    if isinstance(a, torch.Tensor):
+        a = a.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def splitk_merge(o_parts, lse_parts):
+    """Merge of partial results: o_parts [..., S, D], lse_parts [..., S] ->
+    (o [..., D], lse [...])."""
+    op, lp = _f64(o_parts), _f64(lse_parts)
+    S, D = op.shape[-2], op.shape[-1]
+    lead = lp.shape[:-1]
+    n = int(np.prod(lead)) if lead else 1
+    o = np.empty(lead + (D,), dtype=np.float64)
+    lse = np.empty(lead, dtype=np.float64)
+    rc = _load().oracle_splitk_merge(_np_ptr(op), _np_ptr(lp), n, S, D, _np_ptr(o), _np_ptr(lse))
+    if rc:
+        raise ValueError("oracle_splitk_merge: bad arguments")
+    return o, lse
+
+
+def splitk_merge_backward(o_parts, lse_parts, o, lse, d_o, d_lse):
+    """Gradients of splitk_merge: given the partials, the merged (o, lse) and
+    the gradients (d_o, d_lse) of some scalar with respect to them, returns
+    (d_o_parts [..., S, D], d_lse_parts [..., S])."""
+    op, lp, oo, ll, do, dl = (_f64(x) for x in (o_parts, lse_parts, o, lse, d_o, d_lse))
+    S, D = op.shape[-2], op.shape[-1]
+    lead = lp.shape[:-1]
+    n = int(np.prod(lead)) if lead else 1
+    dop = np.empty(op.shape, dtype=np.float64)
+    dlp = np.empty(lp.shape, dtype=np.float64)
+    rc = _load().oracle_splitk_merge_backward(_np_ptr(op), _np_ptr(lp), _np_ptr(oo), _np_ptr(ll), _np_ptr(do),
+                                              _np_ptr(dl), n, S, D, _np_ptr(dop), _np_ptr(dlp))
+    if rc:
+        raise ValueError("oracle_splitk_merge_backward: bad arguments")
+    return dop, dlp

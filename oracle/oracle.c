@@ -26,7 +26,11 @@
  *        paged cache are found through a per-sequence block table;
  *        `_splitK_reduce`: partial results merge as
  *        M = max_s L_s, w_s = exp(L_s - M), O = sum w_s O_s / sum w_s,
- *        L = M + log(sum w_s), and (0, -inf) when every L_s is -inf.
+ *        L = M + log(sum w_s), and (0, -inf) when every L_s is -inf;
+ *        with HAS_ADDITIVE_BIAS a bias block (layout [B, G, H, Mq, N] by
+ *        strides) is added to the scaled scores before the softmax;
+ *        `_splitK_reduce_varargs_backward`: the gradients of that merge with
+ *        respect to the partial results.
  *
  * Every input element is the exact value the GPU receives (fp64, fp32, fp16
  * or bf16 storage), widened to double here; all arithmetic is in double.
@@ -160,12 +164,25 @@ static int64_t kv_index(const kv_view* kv, int64_t t, int d) {
     return kv->dense_base + t * (int64_t)kv->D + d;
 }
 
+/* An additive bias row: the bias of key t is element off + t of p (in
+ * storage format dt); p == NULL means no bias. */
+typedef struct {
+    const void* p;
+    int dt;
+    int64_t off;
+} bias_view;
+
+static const bias_view NO_BIAS = {NULL, 0, 0};
+
 /*
  * Attention of one query over keys t in [lo, hi) that satisfy t < vis_end.
  * Steps, in the order of the definition:
- *   1. s_t = scale * sum_d q_d k_{t,d}
+ *   1. s_t = scale * sum_d q_d k_{t,d}  (+ bias_t when a bias is given: [P4]
+ *      HAS_ADDITIVE_BIAS adds it to the scaled score, in the softmax's
+ *      natural units)
  *   2. visible set V = { t in [lo, hi) : t < vis_end }
- *   3. V empty  -> O = 0, L = -inf
+ *   3. V empty, or every s_t on V is -inf (a bias of -inf masks a key)
+ *      -> O = 0, L = -inf
  *   4. m = max_{t in V} s_t, Z = sum_{t in V} exp(s_t - m), L = m + log Z
  *   5. P_t = exp(s_t - L) on V
  *   6. O = sum_{t in V} P_t v_t
@@ -173,7 +190,7 @@ static int64_t kv_index(const kv_view* kv, int64_t t, int d) {
  * P_t (0 outside V) is stored at p_out[t - lo].
  */
 static void attend_one(const void* q, int64_t q_off, int q_dt, const kv_view* kv,
-                       int64_t lo, int64_t hi, int64_t vis_end, double scale,
+                       int64_t lo, int64_t hi, int64_t vis_end, double scale, bias_view bias,
                        double* s, double* o, double* lse, double* p_out) {
     const int D = kv->D;
     int64_t end = hi < vis_end ? hi : vis_end;
@@ -189,10 +206,12 @@ static void attend_one(const void* q, int64_t q_off, int q_dt, const kv_view* kv
         for (int d = 0; d < D; ++d)
             acc += elem(q, q_off + d, q_dt) * kv_value(kv, kv->k, kv->k_ss, t, d);
         s[t - lo] = scale * acc;
+        if (bias.p) s[t - lo] += elem(bias.p, bias.off + t, bias.dt);
     }
     double m = -INFINITY;
     for (int64_t t = lo; t < end; ++t)
         if (s[t - lo] > m) m = s[t - lo];
+    if (m == -INFINITY) { *lse = m; return; }  /* every visible key masked by the bias */
     double z = 0.0;
     for (int64_t t = lo; t < end; ++t) z += exp(s[t - lo] - m);
     double L = m + log(z);
@@ -244,7 +263,7 @@ int oracle_attn_fwd(const void* q, const void* k, const void* v, int dt,
             kv_view kv = {k, v, dt, D, ((int64_t)b * Hkv + g) * kv_len * (int64_t)D,
                           NULL, 0, Hkv, g, NULL, NULL};
             int64_t vis_end = causal ? i + 1 + delta : (int64_t)kv_len;
-            attend_one(q, r * (int64_t)D, dt, &kv, 0, kv_len, vis_end, scale, s,
+            attend_one(q, r * (int64_t)D, dt, &kv, 0, kv_len, vis_end, scale, NO_BIAS, s,
                        o_out + n * (int64_t)D, lse_out + n, NULL);
         }
         free(s);
@@ -272,7 +291,7 @@ int oracle_softmax_matrix(const void* q, const void* k, int dt,
         double lse;
         int64_t vis_end = causal ? i + 1 + delta : (int64_t)kv_len;
         attend_one(q, (((int64_t)b * Hq + h) * q_len + i) * D, dt, &kv, 0, kv_len, vis_end,
-                   scale, s, o, &lse, p_out + i * (int64_t)kv_len);
+                   scale, NO_BIAS, s, o, &lse, p_out + i * (int64_t)kv_len);
     }
     free(o);
     free(s);
@@ -314,7 +333,7 @@ int oracle_attn_decode(const void* q, const void* k, const void* v, int dt,
             kv_view kv = {k, v, dt, D, ((int64_t)b * Hkv + g) * max_kv_len * (int64_t)D,
                           block_table ? block_table + (int64_t)b * max_pages : NULL,
                           page_size, Hkv, g, NULL, NULL};
-            attend_one(q, r * (int64_t)D, dt, &kv, 0, len, len, scale, s,
+            attend_one(q, r * (int64_t)D, dt, &kv, 0, len, len, scale, NO_BIAS, s,
                        o_out + n * (int64_t)D, lse_out + n, NULL);
         }
         free(s);
@@ -362,7 +381,7 @@ int oracle_attn_decode_multi(const void* q, const void* k, const void* v, int dt
                           page_size, Hkv, g, NULL, NULL};
             /* position of query i: len - q_len + i; keys t <= that position */
             int64_t vis_end = len - q_len + i + 1;
-            attend_one(q, r * (int64_t)D, dt, &kv, 0, len, vis_end, scale, s,
+            attend_one(q, r * (int64_t)D, dt, &kv, 0, len, vis_end, scale, NO_BIAS, s,
                        o_out + n * (int64_t)D, lse_out + n, NULL);
         }
         free(s);
@@ -422,7 +441,7 @@ int oracle_attn_prefill_paged(const void* q, const void* k, const void* v, int d
             int g = h / group;
             kv_view kv = {k, v, dt, D, 0, kv_indices + kv_indptr[b], page_size, Hkv, g, NULL, NULL};
             int64_t vis_end = causal ? i + 1 + (kv_len - q_len) : kv_len;
-            attend_one(q, r * (int64_t)D, dt, &kv, 0, kv_len, vis_end, scale, s,
+            attend_one(q, r * (int64_t)D, dt, &kv, 0, kv_len, vis_end, scale, NO_BIAS, s,
                        o_out + n * (int64_t)D, lse_out + n, NULL);
         }
         free(s);
@@ -468,7 +487,7 @@ int oracle_attn_decode_fp8(const void* q, int q_dt, const void* k, const void* v
             kv_view kv = {k, v, ORACLE_FP8E4M3, D, ((int64_t)b * Hkv + g) * max_kv_len * (int64_t)D,
                           block_table ? block_table + (int64_t)b * max_pages : NULL,
                           page_size, Hkv, g, k_ss, v_ss};
-            attend_one(q, r * (int64_t)D, q_dt, &kv, 0, len, len, scale, s,
+            attend_one(q, r * (int64_t)D, q_dt, &kv, 0, len, len, scale, NO_BIAS, s,
                        o_out + n * (int64_t)D, lse_out + n, NULL);
         }
         free(s);
@@ -521,7 +540,7 @@ int oracle_decode_split_merge(const void* q, const void* k, const void* v, int d
                 if (lo < 0) lo = 0;
                 if (hi > len) hi = len;
                 if (hi < lo) hi = lo;
-                attend_one(q, r * (int64_t)D, dt, &kv, lo, hi, len, scale, s,
+                attend_one(q, r * (int64_t)D, dt, &kv, lo, hi, len, scale, NO_BIAS, s,
                            os + (int64_t)sp * D, ls + sp, NULL);
             }
             /* merge */
@@ -550,4 +569,175 @@ int oracle_decode_split_merge(const void* q, const void* k, const void* v, int d
         free(s);
     }
     return bad;
+}
+
+/*
+ * Forward with an additive attention bias.  [P4] `_fwd_kernel_splitK` with
+ * HAS_ADDITIVE_BIAS: the bias of (b, h, i, j) is added to the scaled score,
+ * s_ij = scale * q_i . k_j + bias(b, h, i, j), before the softmax (the kernel
+ * adds it in its base-2 units, i.e. multiplied by log2 e, which is the same
+ * softmax); the causal rule of oracle_attn_fwd still applies on top.
+ * bias(b, h, i, j) = bias[b * sb + h * sh + i * sq + j] in storage format
+ * bias_dt (strides in elements; a stride of 0 broadcasts).  A row whose
+ * visible scores are all -inf gives (0, -inf).  Layouts and rows as for
+ * oracle_attn_fwd.
+ */
+int oracle_attn_fwd_bias(const void* q, const void* k, const void* v, int dt,
+                         const void* bias, int bias_dt, int64_t sb, int64_t sh, int64_t sq,
+                         int B, int Hq, int Hkv, int q_len, int kv_len, int D,
+                         double scale, int causal,
+                         const int64_t* rows, int64_t n_rows,
+                         double* o_out, double* lse_out) {
+    if (check_fwd_args(B, Hq, Hkv, q_len, kv_len, D) || !bias) return 1;
+    const int64_t total = (int64_t)B * Hq * q_len;
+    if (!rows) n_rows = total;
+    const int group = Hq / Hkv;
+    const int64_t delta = (int64_t)kv_len - q_len;
+    int bad = 0;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)(kv_len > 0 ? kv_len : 1));
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t n = 0; n < n_rows; ++n) {
+            int64_t r = rows ? rows[n] : n;
+            if (r < 0 || r >= total) { bad = 1; continue; }
+            int64_t i = r % q_len;
+            int64_t bh = r / q_len;
+            int h = (int)(bh % Hq);
+            int b = (int)(bh / Hq);
+            const int g = h / group;  /* K/V head of query head h */
+            const int64_t kv_base = ((int64_t)b * Hkv + g) * kv_len * (int64_t)D;
+            kv_view kv = {k, v, dt, D, kv_base, NULL, 0, Hkv, g, NULL, NULL};
+            bias_view bv = {bias, bias_dt, b * sb + h * sh + i * sq};
+            int64_t vis_end = causal ? (i + 1) + delta : (int64_t)kv_len;
+            attend_one(q, r * (int64_t)D, dt, &kv, 0, kv_len, vis_end, scale, bv, s,
+                       o_out + n * (int64_t)D, lse_out + n, NULL);
+        }
+        free(s);
+    }
+    return bad;
+}
+
+/*
+ * Decode (q_len >= 1 queries per sequence, placed and masked as in
+ * oracle_attn_decode_multi) with an additive bias: [P4] `_fwd_kernel_splitK`
+ * with HAS_ADDITIVE_BIAS.  Query i of sequence b, head h, key t gets
+ * bias[b * sb + h * sh + i * sq + t] (storage format bias_dt) added to its
+ * scaled score.  K/V addressing, rows and outputs as for
+ * oracle_attn_decode_multi.
+ */
+int oracle_attn_decode_bias(const void* q, const void* k, const void* v, int dt,
+                            const int* seq_lens, const int* block_table, int max_pages,
+                            int page_size, int B, int Hq, int Hkv, int q_len, int D,
+                            int max_kv_len, double scale,
+                            const void* bias, int bias_dt, int64_t sb, int64_t sh, int64_t sq,
+                            const int64_t* rows, int64_t n_rows,
+                            double* o_out, double* lse_out) {
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv || max_kv_len < 0 || q_len <= 0) return 1;
+    if (block_table && (page_size <= 0 || max_pages <= 0)) return 1;
+    if (!bias) return 1;
+    const int64_t total = (int64_t)B * Hq * q_len;
+    if (!rows) n_rows = total;
+    const int group = Hq / Hkv;
+    int bad = 0;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)(max_kv_len > 0 ? max_kv_len : 1));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t n = 0; n < n_rows; ++n) {
+            int64_t r = rows ? rows[n] : n;
+            if (r < 0 || r >= total) { bad = 1; continue; }
+            int64_t i = r % q_len;
+            int64_t bh = r / q_len;
+            int h = (int)(bh % Hq);
+            int b = (int)(bh / Hq);
+            int g = h / group;
+            int64_t len = seq_lens[b];
+            if (len < 0 || len > max_kv_len) { bad = 1; continue; }
+            kv_view kv = {k, v, dt, D, ((int64_t)b * Hkv + g) * max_kv_len * (int64_t)D,
+                          block_table ? block_table + (int64_t)b * max_pages : NULL,
+                          page_size, Hkv, g, NULL, NULL};
+            bias_view bv = {bias, bias_dt, (int64_t)b * sb + (int64_t)h * sh + i * sq};
+            int64_t vis_end = (len - q_len) + i + 1;  /* query i at position len - q_len + i */
+            attend_one(q, r * (int64_t)D, dt, &kv, 0, len, vis_end, scale, bv, s,
+                       o_out + n * (int64_t)D, lse_out + n, NULL);
+        }
+        free(s);
+    }
+    return bad;
+}
+
+/*
+ * Merge of n_splits partial results per row, [P4] `_splitK_reduce`:
+ * M = max_s L_s, w_s = exp(L_s - M), O = sum_s w_s O_s / sum_s w_s,
+ * L = M + log(sum_s w_s); (0, -inf) when every L_s is -inf.
+ * o_parts [n_rows, n_splits, D], lse_parts [n_rows, n_splits];
+ * o_out [n_rows, D], lse_out [n_rows].
+ */
+int oracle_splitk_merge(const double* o_parts, const double* lse_parts, int64_t n_rows, int n_splits, int D,
+                        double* o_out, double* lse_out) {
+    if (n_rows < 0 || n_splits < 1 || D <= 0) return 1;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < n_rows; ++n) {
+        const double* ls = lse_parts + n * n_splits;
+        const double* os = o_parts + n * (int64_t)n_splits * D;
+        double* o = o_out + n * (int64_t)D;
+        double M = -INFINITY;
+        for (int sp = 0; sp < n_splits; ++sp)
+            if (ls[sp] > M) M = ls[sp];
+        for (int d = 0; d < D; ++d) o[d] = 0.0;
+        if (M == -INFINITY) {
+            lse_out[n] = M;
+            continue;
+        }
+        double wtot = 0.0;
+        for (int sp = 0; sp < n_splits; ++sp) {
+            double wt = exp(ls[sp] - M);
+            wtot += wt;
+            for (int d = 0; d < D; ++d) o[d] += wt * os[(int64_t)sp * D + d];
+        }
+        for (int d = 0; d < D; ++d) o[d] /= wtot;
+        lse_out[n] = log(wtot) + M;
+    }
+    return 0;
+}
+
+/*
+ * Gradients of that merge, [P4] `_splitK_reduce_varargs_backward`.  With the
+ * merged (O, L) of the partials (O_s, L_s) and the incoming gradients dO, dL:
+ * the weight of partial s in O is w_s = exp(L_s - L) (the weights sum to 1),
+ * O = sum_s w_s O_s and L = log sum_s exp(L_s), so
+ *   dO/dO_s = w_s,  dL/dO_s = 0,  dO/dL_s = w_s (O_s - O),  dL/dL_s = w_s,
+ * and by the chain rule
+ *   dO_s = w_s dO,
+ *   dL_s = w_s (dL + sum_d (O_s - O)_d dO_d).
+ * A partial with L_s = -inf (an empty chunk), and every partial of a row
+ * with L = -inf, gets zero gradients.
+ * o_parts / d_o_parts [n_rows, n_splits, D], lse_parts / d_lse_parts
+ * [n_rows, n_splits], o / d_o [n_rows, D], lse / d_lse [n_rows].
+ */
+int oracle_splitk_merge_backward(const double* o_parts, const double* lse_parts, const double* o,
+                                 const double* lse, const double* d_o, const double* d_lse,
+                                 int64_t n_rows, int n_splits, int D,
+                                 double* d_o_parts, double* d_lse_parts) {
+    if (n_rows < 0 || n_splits < 1 || D <= 0) return 1;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < n_rows; ++n) {
+        const double* orow = o + n * (int64_t)D;
+        const double* dorow = d_o + n * (int64_t)D;
+        for (int sp = 0; sp < n_splits; ++sp) {
+            const int64_t ps = n * n_splits + sp;
+            const double* os = o_parts + ps * D;
+            double* dos = d_o_parts + ps * D;
+            const double ls = lse_parts[ps];
+            const double w = (ls == -INFINITY || lse[n] == -INFINITY) ? 0.0 : exp(ls - lse[n]);
+            double dot = 0.0;
+            for (int d = 0; d < D; ++d) {
+                dos[d] = w * dorow[d];
+                dot += (os[d] - orow[d]) * dorow[d];
+            }
+            d_lse_parts[ps] = w == 0.0 ? 0.0 : w * (d_lse[n] + dot);
+        }
+    }
+    return 0;
 }

@@ -484,3 +484,248 @@ def test_decode_fp8_unit_scale_is_plain_decode():
     vb = inp.v8.view(torch.float8_e4m3fn).to(torch.bfloat16)
     o2, l2 = oracle.attn_decode(inp.q, kb, vb, inp.seq_lens, 0.2, block_table=inp.block_table)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+# ---- additive bias (splitk_kernels.py, `_fwd_kernel_splitK` HAS_ADDITIVE_BIAS) ----
+
+def torch_reference_bias(q, k, v, bias, scale, causal):
+    """softmax(scale * Q K^T + bias + mask) V in torch fp64; a row whose
+    visible scores are all -inf gives (0, -inf)."""
+    q, k, v = (t.to(torch.float64) for t in (q, k, v))
+    B, Hq, Lq, D = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    k = k.repeat_interleave(G, dim=1)
+    v = v.repeat_interleave(G, dim=1)
+    s = scale * torch.matmul(q, k.transpose(-1, -2).contiguous()) + bias.to(torch.float64)
+    if causal:
+        i = torch.arange(Lq).view(-1, 1)
+        j = torch.arange(Lk).view(1, -1)
+        s = s.masked_fill(~(j <= i + (Lk - Lq)), float("-inf"))
+    lse = torch.logsumexp(s, dim=-1)
+    empty = torch.isneginf(lse)
+    p = torch.softmax(s, dim=-1)
+    p = torch.where(empty[..., None], torch.zeros_like(p), p)
+    return torch.matmul(p, v).numpy(), lse.numpy()
+
+
+BIAS_SHAPES = [
+    # B, Hq, Hkv, q_len, kv_len, D, causal, bias shape (broadcast dims = 1)
+    (1, 2, 1, 5, 5, 8, True, "full"),
+    (2, 4, 2, 7, 9, 16, False, "full"),
+    (1, 4, 2, 6, 11, 8, True, "per_head"),      # [1, Hq, q_len, kv_len]: shared by the batch
+    (2, 8, 2, 9, 4, 8, True, "per_batch"),      # [B, 1, q_len, kv_len]: shared by the heads
+    (1, 6, 3, 3, 13, 32, False, "keys_only"),   # [1, 1, 1, kv_len]: one row for every query
+]
+
+
+def _bias_of(kind, B, Hq, Lq, Lk, dtype, seed):
+    g = torch.Generator().manual_seed(seed)
+    shape = {"full": (B, Hq, Lq, Lk), "per_head": (1, Hq, Lq, Lk), "per_batch": (B, 1, Lq, Lk),
+             "keys_only": (1, 1, 1, Lk)}[kind]
+    return (2.0 * torch.randn(shape, generator=g)).to(dtype)
+
+
+@pytest.mark.parametrize("shape", BIAS_SHAPES)
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_bias_matches_torch(shape, dtype):
+    B, Hq, Hkv, Lq, Lk, D, causal, kind = shape
+    q, k, v = make_prefill(B, Hq, Hkv, Lq, Lk, D, dtype, seed=Lq * Lk + D)
+    bias = _bias_of(kind, B, Hq, Lq, Lk, q.dtype, seed=D)
+    scale = fp32_scale(D)
+    o, lse = oracle.attn_fwd_bias(q, k, v, bias, scale, causal)
+    o_ref, lse_ref = torch_reference_bias(q, k, v, bias.expand(B, Hq, Lq, Lk), scale, causal)
+    np.testing.assert_allclose(o, o_ref, rtol=0, atol=TOL)
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(fin, np.isfinite(lse))
+    np.testing.assert_allclose(lse[fin], lse_ref[fin], rtol=0, atol=TOL)
+
+
+def test_zero_bias_is_no_bias_bitwise():
+    q, k, v = make_prefill(2, 4, 2, 9, 13, 16, "bf16", seed=3)
+    for causal in (True, False):
+        o1, l1 = oracle.attn_fwd(q, k, v, 0.25, causal)
+        o2, l2 = oracle.attn_fwd_bias(q, k, v, torch.zeros(1, 1, 1, 1), 0.25, causal)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_minus_inf_bias_on_the_causal_pattern_is_causal():
+    # a bias of -inf exactly where the bottom-right rule hides a key, 0 elsewhere,
+    # without the causal flag: the causal result (also for q_len > kv_len rows)
+    for Lq, Lk in ((7, 7), (5, 12), (9, 4)):
+        q, k, v = make_prefill(1, 4, 2, Lq, Lk, 8, "f32", seed=Lq + Lk)
+        i = torch.arange(Lq).view(-1, 1)
+        j = torch.arange(Lk).view(1, -1)
+        bias = torch.where(j <= i + (Lk - Lq), 0.0, float("-inf")).view(1, 1, Lq, Lk)
+        o1, l1 = oracle.attn_fwd(q, k, v, 0.3, True)
+        o2, l2 = oracle.attn_fwd_bias(q, k, v, bias, 0.3, False)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_bias_as_log_weights_with_zero_keys():
+    # K = 0 makes every score 0, so bias_ij = log w_ij gives P_ij = w_ij / sum_j w_ij:
+    # O_i = sum_j w_ij v_j / sum_j w_ij and L_i = log sum_j w_ij (closed form; a
+    # transposed or mis-strided bias index would pick other weights)
+    B, Hq, Hkv, Lq, Lk, D = 2, 4, 2, 5, 9, 8
+    _, _, v = make_prefill(B, Hq, Hkv, Lq, Lk, D, "f32", seed=11)
+    q = torch.randn(B, Hq, Lq, D)
+    k = torch.zeros(B, Hkv, Lk, D)
+    g = torch.Generator().manual_seed(12)
+    w = torch.rand(B, Hq, Lq, Lk, generator=g, dtype=torch.float64) + 0.1
+    o, lse = oracle.attn_fwd_bias(q, k, v, torch.log(w), 0.7, False)
+    vv = v.double().repeat_interleave(Hq // Hkv, dim=1)
+    o_ref = torch.matmul(w, vv) / w.sum(-1, keepdim=True)
+    np.testing.assert_allclose(o, o_ref.numpy(), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, torch.log(w.sum(-1)).numpy(), rtol=0, atol=1e-13)
+
+
+def test_row_constant_bias_shifts_lse_only():
+    q, k, v = make_prefill(1, 4, 2, 6, 10, 16, "f32", seed=21)
+    c = torch.tensor([0.5, -3.0, 7.25, 0.0, 1.0, -0.125], dtype=torch.float64).view(1, 1, 6, 1)
+    o1, l1 = oracle.attn_fwd(q, k, v, 0.2, True)
+    o2, l2 = oracle.attn_fwd_bias(q, k, v, c, 0.2, True)
+    np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l2, l1 + c.view(1, 1, 6).numpy(), rtol=0, atol=1e-13)
+
+
+def test_bias_masking_every_key_gives_empty_row():
+    q, k, v = make_prefill(1, 2, 1, 3, 5, 8, "f32", seed=2)
+    bias = torch.zeros(1, 2, 3, 5)
+    bias[0, 1, 2, :] = float("-inf")
+    o, lse = oracle.attn_fwd_bias(q, k, v, bias, 0.3, False)
+    assert np.all(o[0, 1, 2] == 0) and lse[0, 1, 2] == -np.inf
+    assert np.isfinite(lse[0, 0]).all() and np.isfinite(lse[0, 1, :2]).all()
+
+
+@pytest.mark.parametrize("q_len", [1, 3])
+def test_decode_bias_matches_torch_on_gathered_keys(q_len):
+    inp = make_decode(3, 8, 2, 16, "bf16", seed=31 + q_len, len_lo=1, len_hi=40, page_size=8, q_len=q_len)
+    scale = fp32_scale(16)
+    L = int(inp.seq_lens.max())
+    g = torch.Generator().manual_seed(5)
+    bias = torch.randn(3, 8, q_len, L, generator=g).to(torch.bfloat16)
+    q4 = inp.q if inp.q.dim() == 4 else inp.q.unsqueeze(2)
+    o, lse = oracle.attn_decode_bias(q4, inp.k_cache, inp.v_cache, inp.seq_lens, bias, scale,
+                                     block_table=inp.block_table, max_kv_len=inp.max_kv_len)
+    for b in range(3):
+        n = int(inp.seq_lens[b])
+        pages = inp.block_table[b, :(n + 7) // 8].long()
+        kd = inp.k_cache[pages].reshape(-1, 2, 16)[:n].permute(1, 0, 2).unsqueeze(0)
+        vd = inp.v_cache[pages].reshape(-1, 2, 16)[:n].permute(1, 0, 2).unsqueeze(0)
+        # the q_len queries are the last positions: a causal forward with kv_len = n
+        o_ref, l_ref = torch_reference_bias(q4[b:b + 1], kd, vd, bias[b:b + 1, :, :, :n], scale, True)
+        np.testing.assert_allclose(o[b], o_ref[0], rtol=0, atol=TOL)
+        fin = np.isfinite(l_ref[0])
+        assert np.array_equal(fin, np.isfinite(lse[b]))
+        np.testing.assert_allclose(lse[b][fin], l_ref[0][fin], rtol=0, atol=TOL)
+
+
+def test_decode_bias_equals_prefill_bias_for_one_query():
+    q, k, v = make_prefill(2, 4, 2, 1, 23, 8, "f32", seed=8)
+    bias = torch.randn(2, 4, 1, 23, dtype=torch.float64)
+    o1, l1 = oracle.attn_fwd_bias(q, k, v, bias, 0.4, False)
+    lens = torch.tensor([23, 23], dtype=torch.int32)
+    o2, l2 = oracle.attn_decode_bias(q, k, v, lens, bias, 0.4)
+    np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(l2, l1, rtol=0, atol=1e-15)
+
+
+# ---- merge of partial results and its backward (splitk_kernels.py,
+# `_splitK_reduce` and `_splitK_reduce_varargs_backward`) ----------------------
+
+def _partials(rows, S, D, seed, empty=()):
+    g = np.random.default_rng(seed)
+    op = g.standard_normal((rows, S, D))
+    lp = 3.0 * g.standard_normal((rows, S))
+    for r, s in empty:
+        op[r, s] = 0.0
+        lp[r, s] = -np.inf
+    return op, lp
+
+
+def test_merge_equals_unsplit_attention():
+    # split the keys of plain attention rows into chunks, merge: the unsplit row
+    q, k, v = make_prefill(1, 2, 1, 3, 20, 8, "f32", seed=4)
+    edges = [0, 5, 6, 13, 20]
+    parts = [oracle.attn_fwd(q, k[:, :, a:b], v[:, :, a:b], 0.3, False) for a, b in zip(edges, edges[1:])]
+    op = np.stack([p[0] for p in parts], axis=-2)
+    lp = np.stack([p[1] for p in parts], axis=-1)
+    o, lse = oracle.splitk_merge(op, lp)
+    o_ref, l_ref = oracle.attn_fwd(q, k, v, 0.3, False)
+    np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, l_ref, rtol=0, atol=1e-14)
+
+
+def _objective(op, lp, d_o, d_lse):
+    o, lse = oracle.splitk_merge(op, lp)
+    return float((o * d_o).sum() + (lse * d_lse).sum())
+
+
+def test_merge_backward_matches_finite_differences():
+    rows, S, D = 3, 4, 5
+    op, lp = _partials(rows, S, D, seed=1, empty=[(1, 2)])
+    g = np.random.default_rng(2)
+    d_o, d_lse = g.standard_normal((rows, D)), g.standard_normal(rows)
+    o, lse = oracle.splitk_merge(op, lp)
+    dop, dlp = oracle.splitk_merge_backward(op, lp, o, lse, d_o, d_lse)
+    h = 1e-6
+    for r in range(rows):
+        for s in range(S):
+            if np.isneginf(lp[r, s]):
+                continue
+            for d in range(D):
+                a, b = op.copy(), op.copy()
+                a[r, s, d] += h
+                b[r, s, d] -= h
+                fd = (_objective(a, lp, d_o, d_lse) - _objective(b, lp, d_o, d_lse)) / (2 * h)
+                assert abs(fd - dop[r, s, d]) <= 1e-7 * (1 + abs(fd))
+            a, b = lp.copy(), lp.copy()
+            a[r, s] += h
+            b[r, s] -= h
+            fd = (_objective(op, a, d_o, d_lse) - _objective(op, b, d_o, d_lse)) / (2 * h)
+            assert abs(fd - dlp[r, s]) <= 1e-7 * (1 + abs(fd))
+    # an empty chunk has weight 0 and gets no gradient
+    assert np.all(dop[1, 2] == 0) and dlp[1, 2] == 0
+
+
+def test_merge_backward_sums_and_single_split():
+    rows, S, D = 6, 5, 7
+    op, lp = _partials(rows, S, D, seed=3, empty=[(0, 0), (0, 4), (2, 1)])
+    g = np.random.default_rng(4)
+    d_o, d_lse = g.standard_normal((rows, D)), g.standard_normal(rows)
+    o, lse = oracle.splitk_merge(op, lp)
+    dop, dlp = oracle.splitk_merge_backward(op, lp, o, lse, d_o, d_lse)
+    # the weights sum to 1 and sum_s w_s (O_s - O) = 0: the gradients of the
+    # partials add up to the incoming ones
+    np.testing.assert_allclose(dop.sum(axis=1), d_o, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dlp.sum(axis=1), d_lse, rtol=0, atol=1e-13)
+    # one split: the merge is the identity
+    o1, l1 = oracle.splitk_merge(op[:, :1], lp[:, :1])
+    d1, dl1 = oracle.splitk_merge_backward(op[:, :1], lp[:, :1], o1, l1, d_o, d_lse)
+    fin = np.isfinite(lp[:, 0])
+    np.testing.assert_allclose(d1[fin, 0], d_o[fin], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(dl1[fin, 0], d_lse[fin], rtol=0, atol=1e-15)
+
+
+def test_merge_backward_equal_lse_gives_equal_weights():
+    # S partials with one LSE: w_s = 1/S, dO_s = dO/S, dL_s = (dL + <O_s - O, dO>)/S
+    S, D = 4, 3
+    op = np.arange(S * D, dtype=np.float64).reshape(1, S, D) / 7.0
+    lp = np.full((1, S), 0.75)
+    d_o, d_lse = np.array([[1.0, -2.0, 0.5]]), np.array([0.25])
+    o, lse = oracle.splitk_merge(op, lp)
+    np.testing.assert_allclose(o[0], op[0].mean(axis=0), rtol=0, atol=1e-15)
+    assert abs(lse[0] - (0.75 + math.log(S))) <= 1e-15
+    dop, dlp = oracle.splitk_merge_backward(op, lp, o, lse, d_o, d_lse)
+    np.testing.assert_allclose(dop[0], np.tile(d_o / S, (S, 1)), rtol=0, atol=1e-15)
+    want = (d_lse[0] + ((op[0] - o[0]) * d_o[0]).sum(axis=1)) / S
+    np.testing.assert_allclose(dlp[0], want, rtol=0, atol=1e-14)
+
+
+def test_merge_backward_all_empty_row_is_zero():
+    op, lp = _partials(2, 3, 4, seed=9, empty=[(0, 0), (0, 1), (0, 2)])
+    o, lse = oracle.splitk_merge(op, lp)
+    assert lse[0] == -np.inf and np.all(o[0] == 0)
+    dop, dlp = oracle.splitk_merge_backward(op, lp, o, lse, np.ones((2, 4)), np.ones(2))
+    assert np.all(dop[0] == 0) and np.all(dlp[0] == 0)
+    assert np.isfinite(dop[1]).all() and np.isfinite(dlp[1]).all()

@@ -48,6 +48,26 @@ MUTANTS = {
                                 "return x * half_bits_to_double((uint16_t)(w >> 16)) + half_bits_to_double((uint16_t)(w & 0xffff));"),
     "paged_prefill_top_left": ("int64_t vis_end = causal ? i + 1 + (kv_len - q_len) : kv_len;",
                                "int64_t vis_end = causal ? i + 1 : kv_len;"),
+    "bias_dropped": ("if (bias.p) s[t - lo] += elem(bias.p, bias.off + t, bias.dt);", ";"),
+    "bias_scaled_with_scores": ("if (bias.p) s[t - lo] += elem(bias.p, bias.off + t, bias.dt);",
+                                "if (bias.p) s[t - lo] += scale * elem(bias.p, bias.off + t, bias.dt);"),
+    "bias_query_and_head_strides_swapped": ("bias_view bv = {bias, bias_dt, b * sb + h * sh + i * sq};",
+                                            "bias_view bv = {bias, bias_dt, b * sb + h * sq + i * sh};"),
+    "decode_bias_query_index_dropped": ("bias_view bv = {bias, bias_dt, (int64_t)b * sb + (int64_t)h * sh + i * sq};",
+                                        "bias_view bv = {bias, bias_dt, (int64_t)b * sb + (int64_t)h * sh};"),
+    "bias_fully_masked_row_not_empty": ("if (m == -INFINITY) { *lse = m; return; }", ";"),
+    "merge_standalone_lse_without_max": ("lse_out[n] = log(wtot) + M;", "lse_out[n] = log(wtot);"),
+    "merge_backward_dot_dropped": ("d_lse_parts[ps] = w == 0.0 ? 0.0 : w * (d_lse[n] + dot);",
+                                   "d_lse_parts[ps] = w == 0.0 ? 0.0 : w * d_lse[n];"),
+    "merge_backward_difference_reversed": ("dot += (os[d] - orow[d]) * dorow[d];",
+                                           "dot += (orow[d] - os[d]) * dorow[d];"),
+    "merge_backward_weight_unnormalised": ("exp(ls - lse[n])", "exp(ls)"),
+    "bias_fwd_causal_off_by_one": ("int64_t vis_end = causal ? (i + 1) + delta : (int64_t)kv_len;",
+                                   "int64_t vis_end = causal ? i + delta : (int64_t)kv_len;"),
+    "bias_fwd_head_map_modulo": ("const int g = h / group;  /* K/V head of query head h */",
+                                 "const int g = h % Hkv;  /* K/V head of query head h */"),
+    "decode_bias_position_off_by_one": ("int64_t vis_end = (len - q_len) + i + 1;",
+                                        "int64_t vis_end = (len - q_len) + i;"),
 }
 
 
