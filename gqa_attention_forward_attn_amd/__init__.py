@@ -23,11 +23,11 @@ STATUS = {0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_UNSUPPORTED",
 _TORCH_DT = {torch.float32: GQA_F32, torch.float16: GQA_F16, torch.bfloat16: GQA_BF16}
 
 # Every symbol include/gqa_attn.h declares.
-EXPORTS = ("attn_fwd", "attn_fwd_split", "attn_fwd_split_workspace_bytes", "attn_fwd_kv_splits",
+EXPORTS = ("attn_fwd", "attn_fwd_bias", "attn_fwd_split", "attn_fwd_split_workspace_bytes", "attn_fwd_kv_splits",
            "attn_prefill_paged", "attn_decode_workspace_bytes", "attn_decode_splitk",
            "attn_decode_splitk_fp8",
            "attn_decode_workspace_bytes_multi", "attn_decode_splitk_multi", "attn_decode_splitk_noalloc",
-           "attn_status_str")
+           "attn_decode_splitk_bias", "attn_splitk_merge_backward", "attn_status_str")
 # Every symbol include/gqa_attn_test.h declares (kernel selection for tests).
 TEST_EXPORTS = ("attn_fwd_with_kernel", "attn_prefill_paged_with_kernel")
 # Every symbol include/gqa_ceilings.h declares (measurement kernels).
@@ -56,6 +56,9 @@ def lib() -> ctypes.CDLL:
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32, vp]
     L.attn_fwd.restype = i32
+    i64 = ctypes.c_longlong
+    L.attn_fwd_bias.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32, vp]
+    L.attn_fwd_bias.restype = i32
     L.attn_fwd_with_kernel.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32, i32, vp]
     L.attn_fwd_with_kernel.restype = i32
     L.attn_fwd_split.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32, vp, sz, i32, vp]
@@ -75,6 +78,11 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_splitk.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                      f32, i32, vp, sz, i32, vp]
     L.attn_decode_splitk.restype = i32
+    L.attn_decode_splitk_bias.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                          i32, i32, i32, f32, i32, vp, sz, i32, vp]
+    L.attn_decode_splitk_bias.restype = i32
+    L.attn_splitk_merge_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, vp]
+    L.attn_splitk_merge_backward.restype = i32
     L.attn_decode_splitk_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                              f32, i32, i32, vp]
     L.attn_decode_splitk_noalloc.restype = i32
@@ -197,6 +205,51 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = T
     rc = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, q_len, kv_len, D,
                         sc, int(bool(causal)), dt, _stream(q.device))
     _check("attn_fwd", rc)
+    return out, lse
+
+
+def _bias_strides(bias: torch.Tensor, shape) -> Tuple[int, int, int]:
+    """Element strides (b, h, i) of a bias broadcast to `shape` = (B, H, rows,
+    keys); its last dimension must be contiguous."""
+    if bias.dim() != 4:
+        raise ValueError("bias must be 4-D, broadcastable to " + str(tuple(shape)))
+    try:
+        full = bias.expand(*shape)
+    except RuntimeError as e:
+        raise ValueError(f"bias {tuple(bias.shape)} does not broadcast to {tuple(shape)}") from e
+    if shape[3] > 1 and full.stride(3) != 1:
+        raise ValueError("the bias must be contiguous along the keys")
+    return full.stride(0), full.stride(1), full.stride(2)
+
+
+def attn_fwd_bias(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, bias: torch.Tensor, causal: bool = False,
+                  scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                  lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Attention forward with an additive bias (natural units) added to the
+    scaled scores.  q [B,Hq,q_len,D], k/v [B,Hkv,kv_len,D] (fp16 / bf16); bias in
+    q's dtype, broadcastable to [B, Hq, q_len, kv_len] (size-1 dimensions are
+    read with stride 0), keys contiguous.  Returns (o, lse) as attn_fwd."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k/v must be 4-D: [B, H, len, D]")
+    B, Hq, q_len, D = q.shape
+    Bk, Hkv, kv_len, Dk = k.shape
+    if Bk != B or Dk != D or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("shape mismatch between q, k and v")
+    if q.dtype not in (torch.float16, torch.bfloat16) or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype, float16 or bfloat16")
+    if bias.dtype != q.dtype:
+        raise TypeError("the bias must have q's dtype")
+    sb, sh, sq = _bias_strides(bias, (B, Hq, q_len, kv_len))
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _gpu_contig(name, t, q.device)
+    if not bias.is_cuda or bias.device != q.device:
+        raise ValueError("the bias must be on q's GPU")
+    out = _out_tensor("out", out, q.shape, q.dtype, q.device)
+    lse = _out_tensor("lse", lse, (B, Hq, q_len), torch.float32, q.device)
+    sc = default_scale(D) if scale is None else float(scale)
+    rc = lib().attn_fwd_bias(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), sb, sh, sq, _ptr(out), _ptr(lse), B, Hq, Hkv,
+                             q_len, kv_len, D, sc, int(bool(causal)), _TORCH_DT[q.dtype], _stream(q.device))
+    _check("attn_fwd_bias", rc)
     return out, lse
 
 
@@ -515,3 +568,70 @@ def ceiling_stream_read(src: torch.Tensor, n_workgroups: int, out: Optional[torc
     if rc:
         raise RuntimeError(f"gqa_ceiling_stream_read failed ({rc})")
     return out
+
+
+def attn_decode_splitk_bias(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens: torch.Tensor,
+                            bias: torch.Tensor, block_table: Optional[torch.Tensor] = None, n_splits: int = 16,
+                            scale: Optional[float] = None, max_kv_len: Optional[int] = None,
+                            workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                            lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Split-K decode of q_len queries per sequence (q [B,Hq,q_len,D], as
+    attn_decode_splitk_multi) with an additive bias: query i of sequence b,
+    head h, key t gets bias[b, h, i, t] (natural units, q's dtype).  bias is
+    broadcastable to [B, Hq, q_len, L] with L >= every sequence length, keys
+    contiguous, even strides; rows of an odd length need one readable element
+    past it.  Returns (o [B,Hq,q_len,D], lse [B,Hq,q_len] fp32)."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, Hq, q_len, D]")
+    B, Hq, q_len, D = q.shape
+    Hkv, page_size, max_pages, max_kv_len = _decode_geometry(q, k, v, seq_lens, block_table, max_kv_len, q.dtype)
+    if bias.dtype != q.dtype:
+        raise TypeError("the bias must have q's dtype")
+    sb, sh, sq = _bias_strides(bias, (B, Hq, q_len, bias.shape[-1]))
+    if (sb | sh | sq) & 1 or bias.data_ptr() % 4:
+        raise ValueError("the bias needs even strides and a 4-byte aligned start (keys are read in pairs)")
+    if not bias.is_cuda or bias.device != q.device:
+        raise ValueError("the bias must be on q's GPU")
+    if check_tables:
+        check_decode_tables(seq_lens, block_table, page_size, k.shape[0], max_kv_len)
+        if int(seq_lens.max()) > bias.shape[-1]:
+            raise ValueError("the bias has fewer keys than a sequence")
+    workspace = _workspace(workspace, decode_workspace_bytes_multi(B, Hq, q_len, D, n_splits), q.device)
+    out = _out_tensor("out", out, q.shape, q.dtype, q.device)
+    lse = _out_tensor("lse", lse, (B, Hq, q_len), torch.float32, q.device)
+    sc = default_scale(D) if scale is None else float(scale)
+    rc = lib().attn_decode_splitk_bias(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), sb, sh, sq, _ptr(out), _ptr(lse),
+                                       _ptr(seq_lens), _ptr(block_table), max_pages, page_size, B, Hq, Hkv, q_len, D,
+                                       max_kv_len, sc, int(n_splits), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _TORCH_DT[q.dtype],
+                                       _stream(q.device))
+    _check("attn_decode_splitk_bias", rc)
+    return out, lse
+
+
+def attn_splitk_merge_backward(o_parts: torch.Tensor, lse_parts: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+                               d_o: torch.Tensor, d_lse: torch.Tensor, d_o_parts: Optional[torch.Tensor] = None,
+                               d_lse_parts: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Gradients of the split-K merge with respect to its partials (fp32):
+    o_parts [..., S, D], lse_parts [..., S], o / d_o [..., D], lse / d_lse [...].
+    Returns (d_o_parts [..., S, D], d_lse_parts [..., S])."""
+    if o_parts.dim() < 2:
+        raise ValueError("o_parts must be [..., n_splits, D]")
+    S, D = o_parts.shape[-2], o_parts.shape[-1]
+    lead = tuple(o_parts.shape[:-2])
+    want = {"lse_parts": (lse_parts, lead + (S,)), "o": (o, lead + (D,)), "lse": (lse, lead),
+            "d_o": (d_o, lead + (D,)), "d_lse": (d_lse, lead)}
+    for name, (t, shape) in want.items():
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be {shape}, got {tuple(t.shape)}")
+    for name, t in [("o_parts", o_parts)] + [(n, t) for n, (t, _) in want.items()]:
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+        _gpu_contig(name, t, o_parts.device)
+    d_o_parts = _out_tensor("d_o_parts", d_o_parts, o_parts.shape, torch.float32, o_parts.device)
+    d_lse_parts = _out_tensor("d_lse_parts", d_lse_parts, lse_parts.shape, torch.float32, o_parts.device)
+    rows = int(math.prod(lead)) if lead else 1
+    rc = lib().attn_splitk_merge_backward(_ptr(o_parts), _ptr(lse_parts), _ptr(o), _ptr(lse), _ptr(d_o), _ptr(d_lse),
+                                          _ptr(d_o_parts), _ptr(d_lse_parts), rows, S, D, _stream(o_parts.device))
+    _check("attn_splitk_merge_backward", rc)
+    return d_o_parts, d_lse_parts

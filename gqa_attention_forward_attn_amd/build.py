@@ -17,7 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJ_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libgqa_attn.so")
-SOURCES = ["prefill_fwd.hip", "prefill_pp.hip", "decode_splitk.hip", "ceilings.hip", "scratch.hip", "api.cpp"]
+SOURCES = ["prefill_fwd.hip", "prefill_pp.hip", "decode_splitk.hip", "merge_bwd.hip", "ceilings.hip", "scratch.hip",
+           "api.cpp"]
 # per-source compiler options (none at present)
 EXTRA_FLAGS: dict = {}
 

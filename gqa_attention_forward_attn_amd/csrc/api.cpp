@@ -85,6 +85,42 @@ gqa_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, floa
                                 hip_stream);
 }
 
+gqa_status_t attn_fwd_bias(const void* q, const void* k, const void* v, const void* bias, long long bias_stride_b,
+                           long long bias_stride_h, long long bias_stride_q, void* o, float* lse, int B, int Hq,
+                           int Hkv, int q_len, int kv_len, int D, float scale, int causal, gqa_dtype_t dtype,
+                           void* hip_stream) {
+    if (B < 0 || q_len < 0 || kv_len < 0 || Hq <= 0 || Hkv <= 0 || D <= 0) return GQA_ERR_INVALID_ARG;
+    if (Hq % Hkv != 0) return GQA_ERR_INVALID_ARG;
+    if (!valid_dtype(dtype)) return GQA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return GQA_ERR_INVALID_ARG;
+    if (bias_stride_b < 0 || bias_stride_h < 0 || bias_stride_q < 0) return GQA_ERR_INVALID_ARG;
+    if (!supported_head_dim(D) || dtype == GQA_F32) return GQA_ERR_UNSUPPORTED;
+    if (B == 0 || q_len == 0) return GQA_OK;
+    if (kv_len == 0)  // no key: every row is (0, -inf), the bias is not read
+        return attn_fwd_with_kernel(q, k, v, o, lse, B, Hq, Hkv, q_len, 0, D, scale, causal, dtype, 2, hip_stream);
+    if (!q || !k || !v || !o || !lse || !bias) return GQA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(o) || !aligned16(k) || !aligned16(v)) return GQA_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(bias) & 1u) return GQA_ERR_INVALID_ARG;
+    const long long rows_q = (long long)B * Hq * q_len;
+    const long long rows_kv = (long long)B * Hkv * kv_len;
+    if (rows_q > (1LL << 40) || rows_kv > (1LL << 40)) return GQA_ERR_INVALID_ARG;
+
+    gqa::PrefillArgs a{};
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.q_len = q_len; a.kv_len = kv_len;
+    a.group = Hq / Hkv;
+    a.delta = kv_len - q_len;
+    a.c = scale * kLog2e;
+    a.bias = static_cast<const uint16_t*>(bias);
+    a.bias_sb = bias_stride_b;
+    a.bias_sh = bias_stride_h;
+    a.bias_sq = bias_stride_q;
+    a.bias_k = 1.f / scale;
+    hipError_t e = gqa::launch_prefill_bias(a, D, causal != 0, to_kernel_dtype(dtype),
+                                            static_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
 int attn_fwd_kv_splits(int B, int Hq, int Hkv, int q_len, int kv_len, int D, int causal, gqa_dtype_t dtype) {
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || q_len <= 0 || kv_len <= 0 || Hq % Hkv != 0) return 1;
     if (!supported_head_dim(D) || (dtype != GQA_BF16 && dtype != GQA_F16)) return 1;
@@ -205,19 +241,24 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int D, int n_splits) {
     return attn_decode_workspace_bytes_multi(B, Hq, 1, D, n_splits);
 }
 
-gqa_status_t attn_decode_splitk_multi(const void* q, const void* k, const void* v, void* o, float* lse,
-                                      const int* seq_lens, const int* block_table,
-                                      int max_pages_per_seq, int page_size,
-                                      int B, int Hq, int Hkv, int q_len, int D, int max_kv_len,
-                                      float scale, int n_splits,
-                                      void* workspace, size_t workspace_bytes,
-                                      gqa_dtype_t dtype, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// The 16-bit split-K decode with or without an additive bias (bias == nullptr).
+gqa_status_t decode_16bit(const void* q, const void* k, const void* v, const void* bias, long long bias_sb,
+                          long long bias_sh, long long bias_sq, void* o, float* lse, const int* seq_lens,
+                          const int* block_table, int max_pages_per_seq, int page_size, int B, int Hq, int Hkv,
+                          int q_len, int D, int max_kv_len, float scale, int n_splits, void* workspace,
+                          size_t workspace_bytes, gqa_dtype_t dtype, void* hip_stream, bool with_bias) {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || max_kv_len < 0) return GQA_ERR_INVALID_ARG;
     if (q_len < 1 || q_len > 256) return GQA_ERR_INVALID_ARG;
     if (Hq % Hkv != 0) return GQA_ERR_INVALID_ARG;
     if (n_splits < 1 || n_splits > 256) return GQA_ERR_INVALID_ARG;
     if (!valid_dtype(dtype)) return GQA_ERR_INVALID_ARG;
     if (!std::isfinite(scale) || !(scale > 0.f)) return GQA_ERR_INVALID_ARG;
+    if (with_bias && (bias_sb < 0 || bias_sh < 0 || bias_sq < 0 || (bias_sb | bias_sh | bias_sq) & 1))
+        return GQA_ERR_INVALID_ARG;
     int page_shift = 0;
     if (block_table) {
         if (page_size <= 0 || (page_size & (page_size - 1)) != 0 || max_pages_per_seq <= 0)
@@ -228,6 +269,7 @@ gqa_status_t attn_decode_splitk_multi(const void* q, const void* k, const void* 
     if (!supported_head_dim(D) || dtype == GQA_F32) return GQA_ERR_UNSUPPORTED;
     if (B == 0) return GQA_OK;
     if (!q || !k || !v || !o || !lse || !seq_lens) return GQA_ERR_INVALID_ARG;
+    if (with_bias && (!bias || (reinterpret_cast<uintptr_t>(bias) & 3u))) return GQA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return GQA_ERR_INVALID_ARG;
     if ((long long)B * Hq * q_len > 0x7fffffffLL) return GQA_ERR_INVALID_ARG;
     const size_t need = attn_decode_workspace_bytes_multi(B, Hq, q_len, D, n_splits);
@@ -246,8 +288,42 @@ gqa_status_t attn_decode_splitk_multi(const void* q, const void* k, const void* 
     a.max_kv_len = max_kv_len;
     a.n_splits = n_splits;
     a.c = scale * kLog2e;
+    if (with_bias) {
+        a.bias = static_cast<const uint16_t*>(bias);
+        a.bias_sb = bias_sb;
+        a.bias_sh = bias_sh;
+        a.bias_sq = bias_sq;
+        a.bias_k = 1.f / scale;
+    }
     hipError_t e = gqa::launch_decode(a, to_kernel_dtype(dtype), static_cast<hipStream_t>(hip_stream));
     return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+gqa_status_t attn_decode_splitk_multi(const void* q, const void* k, const void* v, void* o, float* lse,
+                                      const int* seq_lens, const int* block_table,
+                                      int max_pages_per_seq, int page_size,
+                                      int B, int Hq, int Hkv, int q_len, int D, int max_kv_len,
+                                      float scale, int n_splits,
+                                      void* workspace, size_t workspace_bytes,
+                                      gqa_dtype_t dtype, void* hip_stream) {
+    return decode_16bit(q, k, v, nullptr, 0, 0, 0, o, lse, seq_lens, block_table, max_pages_per_seq, page_size, B,
+                        Hq, Hkv, q_len, D, max_kv_len, scale, n_splits, workspace, workspace_bytes, dtype,
+                        hip_stream, false);
+}
+
+gqa_status_t attn_decode_splitk_bias(const void* q, const void* k, const void* v, const void* bias,
+                                     long long bias_stride_b, long long bias_stride_h, long long bias_stride_q,
+                                     void* o, float* lse, const int* seq_lens, const int* block_table,
+                                     int max_pages_per_seq, int page_size, int B, int Hq, int Hkv, int q_len, int D,
+                                     int max_kv_len, float scale, int n_splits, void* workspace,
+                                     size_t workspace_bytes, gqa_dtype_t dtype, void* hip_stream) {
+    return decode_16bit(q, k, v, bias, bias_stride_b, bias_stride_h, bias_stride_q, o, lse, seq_lens, block_table,
+                        max_pages_per_seq, page_size, B, Hq, Hkv, q_len, D, max_kv_len, scale, n_splits, workspace,
+                        workspace_bytes, dtype, hip_stream, true);
 }
 
 gqa_status_t attn_decode_splitk_fp8(const void* q, const void* k_cache, const void* v_cache,
@@ -327,6 +403,21 @@ gqa_status_t attn_decode_splitk_noalloc(const void* q, const void* k, const void
     }
     return attn_decode_splitk(q, k, v, o, lse, seq_lens, block_table, max_pages_per_seq, page_size, B, Hq, Hkv,
                               D, max_kv_len, scale, n_splits, ws, ws_bytes, dtype, hip_stream);
+}
+
+gqa_status_t attn_splitk_merge_backward(const float* o_parts, const float* lse_parts, const float* o,
+                                        const float* lse, const float* d_o, const float* d_lse, float* d_o_parts,
+                                        float* d_lse_parts, long long rows, int n_splits, int D, void* hip_stream) {
+    if (rows < 0 || n_splits < 1 || n_splits > 65536 || D < 1 || D > gqa::merge_backward_max_dims())
+        return GQA_ERR_INVALID_ARG;
+    if (rows == 0) return GQA_OK;
+    if (rows > (1LL << 36)) return GQA_ERR_INVALID_ARG;
+    const void* ptrs[8] = {o_parts, lse_parts, o, lse, d_o, d_lse, d_o_parts, d_lse_parts};
+    for (const void* p : ptrs)
+        if (!p || (reinterpret_cast<uintptr_t>(p) & 3u)) return GQA_ERR_INVALID_ARG;
+    gqa::MergeBwdArgs a{o_parts, lse_parts, o, lse, d_o, d_lse, d_o_parts, d_lse_parts, rows, n_splits, D};
+    hipError_t e = gqa::launch_merge_backward(a, static_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 
 const char* attn_status_str(gqa_status_t s) {

@@ -94,6 +94,14 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
                          : "m0", "memory");
 }
 
+// 4 bytes per lane from global memory into LDS (lane i -> lds + 4 i).
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds) {
+    __asm__ __volatile__("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+                         :
+                         : "v"(gptr), "s"(lds)
+                         : "m0", "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -144,6 +152,12 @@ __device__ __forceinline__ f32x4 mfma16x16(f16_tag, u32x2 a, u32x2 b, f32x4 c) {
                                                   c, 0, 0, 0);
 }
 
+// A stored 16-bit value of the input dtype as fp32.
+__device__ __forceinline__ float bias_to_f32(bf16_tag, uint32_t u16) { return __builtin_bit_cast(float, u16 << 16); }
+__device__ __forceinline__ float bias_to_f32(f16_tag, uint32_t u16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)u16);
+}
+
 __device__ __forceinline__ float lane_value(float x, int src_lane) {
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src_lane << 2, __builtin_bit_cast(int, x)));
 }
@@ -163,19 +177,24 @@ __device__ __forceinline__ int swz(int r) {
     return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
 }
 
-template <class TAG, int D, int NW, int NST, int PG>
+// BIAS: the additive bias of `_fwd_kernel_splitK` (HAS_ADDITIVE_BIAS).  Each
+// slice also brings the bias of its 16 tokens for the block's 16 columns
+// (pairs of keys per 4-byte direct load, 512 bytes after the V slice), added
+// to the scores before the softmax.
+template <class TAG, int D, int NW, int NST, int PG, bool BIAS = false>
 __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) {
     constexpr int ROWB = 2 * D;             // bytes per K/V/q row
     constexpr int CPR = ROWB / 16;          // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;           // rows per direct-load instruction
     constexpr int NI = kSlice / RPI;        // direct loads per slice, each of K and V
     constexpr int SLB = kSlice * ROWB;      // bytes of a K (or V) slice
-    constexpr int STB = 2 * SLB;            // stage: K slice, then V slice
+    constexpr int BSB = BIAS ? 16 * kSlice * 2 : 0;  // bias of a slice: 16 columns x 16 keys
+    constexpr int STB = 2 * SLB + BSB;      // stage: K slice, V slice[, bias]
     constexpr int QB = 16 * ROWB;           // q rows of the head block
     constexpr int WAVEB = QB + NST * STB;   // LDS per wave
     constexpr int KS = D / 32;              // k-steps of S^T = K q^T
     constexpr int NB = D / 16;              // 16-column blocks of O
-    constexpr int PER_SLICE = 2 * NI;
+    constexpr int PER_SLICE = 2 * NI + (BIAS ? 2 : 0);
     static_assert((NST - 1) * PER_SLICE < 64, "vmcnt range");
     static_assert((NST & (NST - 1)) == 0, "NST must be a power of two");
     static_assert(NW * 16 * (D + 3) * 4 <= NW * WAVEB, "merge buffers must fit in the ring");
@@ -238,10 +257,29 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
     // per-lane byte offset; rows past the chunk repeat its last row
     const char* kbytes = static_cast<const char*>(a.k);
     const char* vbytes = static_cast<const char*>(a.v);
+    // BIAS: lane i of bias load j brings keys (2 (i % 8), +1) of column 8 j + i / 8
+    // (columns past the block repeat its last one); its row of the bias
+    [[maybe_unused]] const uint16_t* brow[2];
+    if constexpr (BIAS) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int qr = hb * 16 + min(8 * j + lane / 8, nh - 1);  // query row in the group
+            const int h = g * a.group + qr / a.q_len, qi = qr % a.q_len;
+            brow[j] = a.bias + (long long)b * a.bias_sb + (long long)h * a.bias_sh + (long long)qi * a.bias_sq;
+        }
+    }
     auto issue = [&](int k) {
         const int T = T0 + stride * k;
         const uint32_t st = __builtin_amdgcn_readfirstlane(wlds_u + QB + (k & (NST - 1)) * STB);
         const int last = hi - 1 - T;  // rows of the slice at or past `last` repeat row `last`
+        if constexpr (BIAS) {
+            // key pairs past the chunk read the pair of its last key; that pair
+            // may hold one key past the sequence (rows are readable up to an
+            // even key count)
+            const int t = T + min(2 * (lane & 7), last & ~1);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) dma4(brow[j] + t, st + 2 * SLB + j * 256);
+        }
         if (PG == kPagedSmall) {
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
@@ -328,6 +366,15 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) sc = mfma16x32(TAG(), lds16(st + koff[ks]), qop[ks], sc);
 
+            if constexpr (BIAS) {
+                // this lane's column and keys 4 kq .. 4 kq + 3: s * c gains log2(e) * bias
+                const u32x2 w = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(
+                    st + 2 * SLB + hrow * 32 + kq * 8);
+                sc[0] = fmaf(bias_to_f32(TAG(), w[0] & 0xffffu), a.bias_k, sc[0]);
+                sc[1] = fmaf(bias_to_f32(TAG(), w[0] >> 16), a.bias_k, sc[1]);
+                sc[2] = fmaf(bias_to_f32(TAG(), w[1] & 0xffffu), a.bias_k, sc[2]);
+                sc[3] = fmaf(bias_to_f32(TAG(), w[1] >> 16), a.bias_k, sc[3]);
+            }
             const int T = T0 + stride * k;
             if (T + kSlice > lim_lo) {  // ragged last slice of the chunk, or keys past a query
                 const int tok = T + 4 * kq;
@@ -429,13 +476,6 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
 // 1), and the V slice is converted once into a 16-bit slice buffer that the
 // transposed reads of the P.V product use as in decode_split_kernel.
 
-// 4 bytes per lane from global memory into LDS (lane i -> lds + 4 i).
-__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds) {
-    __asm__ __volatile__("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
-                         :
-                         : "v"(gptr), "s"(lds)
-                         : "m0", "memory");
-}
 
 // Four E4M3 bytes (one dword, element order = byte order) -> four 16-bit floats.
 __device__ __forceinline__ u32x2 e4m3x4_to16(bf16_tag, uint32_t w) {
@@ -801,12 +841,12 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     if (lane == 0) a.lse[row] = W > 0.f ? M + fast_log2(W) * kLn2 : -INFINITY;
 }
 
-template <class TAG, int D, int PG>
+template <class TAG, int D, int PG, bool BIAS = false>
 hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
     const long long n_hb = ((long long)a.group * a.q_len + 15) / 16;
     const long long blocks = (long long)a.B * a.Hkv * n_hb * a.n_splits;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((decode_split_kernel<TAG, D, DEC_NW, DEC_NST, PG>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((decode_split_kernel<TAG, D, DEC_NW, DEC_NST, PG, BIAS>), dim3((unsigned)blocks),
                        dim3(DEC_NW * 64), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -838,17 +878,21 @@ hipError_t dispatch_fp8(const DecodeArgs& a, hipStream_t stream) {
     return paged ? launch_split_fp8<TAG, 128, kPaged>(a, stream) : launch_split_fp8<TAG, 128, kDense>(a, stream);
 }
 
-template <class TAG, int D>
+template <class TAG, int D, bool BIAS>
 hipError_t dispatch_layout(const DecodeArgs& a, hipStream_t stream) {
-    if (a.block_table == nullptr) return launch_split<TAG, D, kDense>(a, stream);
-    if (a.page_shift >= 4) return launch_split<TAG, D, kPaged>(a, stream);
-    return launch_split<TAG, D, kPagedSmall>(a, stream);
+    if (a.block_table == nullptr) return launch_split<TAG, D, kDense, BIAS>(a, stream);
+    if (a.page_shift >= 4) return launch_split<TAG, D, kPaged, BIAS>(a, stream);
+    return launch_split<TAG, D, kPagedSmall, BIAS>(a, stream);
 }
 
 template <class TAG>
 hipError_t dispatch_d(const DecodeArgs& a, hipStream_t stream) {
-    if (a.D == 64) return dispatch_layout<TAG, 64>(a, stream);
-    return dispatch_layout<TAG, 128>(a, stream);
+    if (a.bias) {
+        if (a.D == 64) return dispatch_layout<TAG, 64, true>(a, stream);
+        return dispatch_layout<TAG, 128, true>(a, stream);
+    }
+    if (a.D == 64) return dispatch_layout<TAG, 64, false>(a, stream);
+    return dispatch_layout<TAG, 128, false>(a, stream);
 }
 
 }  // namespace

@@ -39,6 +39,12 @@ struct PrefillArgs {
     const int* kv_indices;        // page ids
     const int* kv_last_page_len;  // [B] tokens in each last page, or nullptr (full pages)
     int page_shift;               // log2(page_size)
+    // Additive bias (four-wave kernel, dense only): bias(b, h, i, j) =
+    // bias[b * bias_sb + h * bias_sh + i * bias_sq + j] in the input dtype,
+    // added to the scores in the softmax's natural units; bias_k = 1 / scale.
+    const uint16_t* bias;
+    long long bias_sb, bias_sh, bias_sq;
+    float bias_k;
 };
 
 // bf16 / fp16 prefill kernel: chosen by shape, or forced (tests).
@@ -46,6 +52,8 @@ enum class PrefillKernel { kAuto, kPingPong, kFourWave };
 
 // Validated arguments only.  D in {64, 128}; dtype one of kDtype*.
 hipError_t launch_prefill(PrefillArgs a, int D, bool causal, int dtype, PrefillKernel kernel, hipStream_t stream);
+// The same with the additive bias of a.bias (bf16 / fp16, four-wave kernel).
+hipError_t launch_prefill_bias(PrefillArgs a, int D, bool causal, int dtype, hipStream_t stream);
 // Ragged batch of requests over a paged K/V cache (bf16 / fp16): the ping-pong
 // kernel for batches that give every CU a workgroup, else the four-wave kernel
 // (or the one `kernel` forces).
@@ -79,6 +87,12 @@ struct DecodeArgs {
     int max_kv_len;           // dense row stride in tokens
     int n_splits;
     float c;                  // scale * log2(e)
+    // Additive bias (16-bit cache only) or nullptr: query i of sequence b, head
+    // h, key t gets bias[b * bias_sb + h * bias_sh + i * bias_sq + t] (input
+    // dtype; even strides, 4-byte aligned); bias_k = 1 / scale.
+    const uint16_t* bias;
+    long long bias_sb, bias_sh, bias_sq;
+    float bias_k;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream);
@@ -89,5 +103,23 @@ size_t scratch_capacity_bytes();
 hipError_t scratch_device_ptr(void** out);
 // K/V as E4M3 bytes with scale-shift words (q_len = 1; pages of >= 16 tokens or dense).
 hipError_t launch_decode_fp8(const DecodeArgs& a, int dtype, hipStream_t stream);
+
+// Backward of the split-K merge (fp32): partials [rows, n_splits, D] and
+// [rows, n_splits], merged results and their gradients [rows, D] and [rows].
+struct MergeBwdArgs {
+    const float* o_parts;
+    const float* lse_parts;
+    const float* o;
+    const float* lse;
+    const float* d_o;
+    const float* d_lse;
+    float* d_o_parts;
+    float* d_lse_parts;
+    long long rows;
+    int n_splits, D;
+};
+
+int merge_backward_max_dims();
+hipError_t launch_merge_backward(const MergeBwdArgs& a, hipStream_t stream);
 
 }  // namespace gqa

@@ -44,7 +44,17 @@ namespace {
 // Growth of a row max (log2 units) that triggers a rescale of acc and l.
 constexpr float kRescaleLog2 = 8.f;
 
-template <class TAG, int D, bool CAUSAL, int NH, bool PAGED>
+// A stored 16-bit value of the input dtype as fp32.
+__device__ __forceinline__ float to_f32(bf16_tag, uint32_t u16) { return __builtin_bit_cast(float, u16 << 16); }
+__device__ __forceinline__ float to_f32(f16_tag, uint32_t u16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)u16);
+}
+
+// BIAS: 0 = none; otherwise the additive bias of splitk_kernels.py
+// (`_fwd_kernel_splitK`, HAS_ADDITIVE_BIAS) is loaded for every score tile and
+// added before the softmax.  BIAS = 4: rows 8-byte aligned, four keys per load
+// (whole tiles; the tail tile reads key by key); BIAS = 1: key by key.
+template <class TAG, int D, bool CAUSAL, int NH, bool PAGED, int BIAS = 0>
 __global__ __launch_bounds__(256, 2) void prefill_fwd_mfma(PrefillArgs a) {
     constexpr int BN = 64;                 // keys per tile
     constexpr int WPH = 4 / NH;            // waves per head
@@ -252,6 +262,34 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_mfma(PrefillArgs a) {
             const uint16_t* ks = smem + buf * (KT + VT);
             const uint16_t* vs = ks + KT;
 
+            // additive bias of this lane's scores (row q_row, keys as in s below);
+            // keys past the last one read the last one (they are masked)
+            [[maybe_unused]] float bv[2][16];
+            if constexpr (BIAS != 0) {
+                const uint16_t* brow = a.bias + (long long)b * a.bias_sb + (long long)h * a.bias_sh +
+                                       (long long)q_row * a.bias_sq;
+                if (BIAS == 4 && t0 + BN <= kv_len) {
+#pragma unroll
+                    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const u32x2 w = *reinterpret_cast<const u32x2*>(brow + t0 + kh * 32 + 8 * j + 4 * half);
+                            bv[kh][4 * j] = to_f32(TAG(), w[0] & 0xffffu);
+                            bv[kh][4 * j + 1] = to_f32(TAG(), w[0] >> 16);
+                            bv[kh][4 * j + 2] = to_f32(TAG(), w[1] & 0xffffu);
+                            bv[kh][4 * j + 3] = to_f32(TAG(), w[1] >> 16);
+                        }
+                } else {
+#pragma unroll
+                    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int key = min(t0 + kh * 32 + 8 * (r >> 2) + 4 * half + (r & 3), last_key);
+                            bv[kh][r] = to_f32(TAG(), brow[key]);
+                        }
+                }
+            }
+
             // S^T[key][query] for 64 keys (two 32-key halves)
             f32x16 s[2];
 #pragma unroll
@@ -266,6 +304,14 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_mfma(PrefillArgs a) {
                     vec8 ka = *reinterpret_cast<const vec8*>(ks + (kh * 32 + l32) * KS + ds * 16 + half * 8);
                     s[kh] = mfma_32x32x16(ka, qf[ds], s[kh]);
                 }
+            }
+
+            if constexpr (BIAS != 0) {
+                // s * c = scale * log2(e) * q.k + log2(e) * bias with bias_k = 1 / scale
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) s[kh][r] = fmaf(bv[kh][r], a.bias_k, s[kh][r]);
             }
 
             if (t0 + BN > wave_full_end) {  // diagonal or tail tile: apply the mask
@@ -514,23 +560,32 @@ __global__ __launch_bounds__(256) void prefill_fwd_f32(PrefillArgs a) {
     }
 }
 
-template <class TAG, int D, bool CAUSAL, int NH, bool PAGED>
+template <class TAG, int D, bool CAUSAL, int NH, bool PAGED, int BIAS = 0>
 hipError_t launch_mfma(PrefillArgs a, hipStream_t stream) {
     constexpr int POS = 32 * (4 / NH);
     a.n_pos_tiles = (a.q_len + POS - 1) / POS;
     a.n_rest = a.B * a.Hkv * (a.group / NH);
     const long long blocks = (long long)a.n_pos_tiles * a.n_rest;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((prefill_fwd_mfma<TAG, D, CAUSAL, NH, PAGED>), dim3((unsigned)blocks), dim3(256), 0,
+    hipLaunchKernelGGL((prefill_fwd_mfma<TAG, D, CAUSAL, NH, PAGED, BIAS>), dim3((unsigned)blocks), dim3(256), 0,
                        stream, a);
     return hipGetLastError();
 }
 
-template <class TAG, int D, bool CAUSAL, bool PAGED = false>
+template <class TAG, int D, bool CAUSAL, bool PAGED = false, int BIAS = 0>
 hipError_t dispatch_nh(PrefillArgs a, hipStream_t stream) {
-    if (a.group % 4 == 0) return launch_mfma<TAG, D, CAUSAL, 4, PAGED>(a, stream);
-    if (a.group % 2 == 0) return launch_mfma<TAG, D, CAUSAL, 2, PAGED>(a, stream);
-    return launch_mfma<TAG, D, CAUSAL, 1, PAGED>(a, stream);
+    if (a.group % 4 == 0) return launch_mfma<TAG, D, CAUSAL, 4, PAGED, BIAS>(a, stream);
+    if (a.group % 2 == 0) return launch_mfma<TAG, D, CAUSAL, 2, PAGED, BIAS>(a, stream);
+    return launch_mfma<TAG, D, CAUSAL, 1, PAGED, BIAS>(a, stream);
+}
+
+template <class TAG, int BIAS>
+hipError_t dispatch_d_bias(PrefillArgs a, int D, bool causal, hipStream_t stream) {
+    if (D == 64)
+        return causal ? dispatch_nh<TAG, 64, true, false, BIAS>(a, stream)
+                      : dispatch_nh<TAG, 64, false, false, BIAS>(a, stream);
+    return causal ? dispatch_nh<TAG, 128, true, false, BIAS>(a, stream)
+                  : dispatch_nh<TAG, 128, false, false, BIAS>(a, stream);
 }
 
 template <int D, bool CAUSAL>
@@ -597,6 +652,15 @@ hipError_t launch_prefill(PrefillArgs a, int D, bool causal, int dtype, PrefillK
         if (D == 64) return causal ? launch_f32<64, true>(a, stream) : launch_f32<64, false>(a, stream);
         return causal ? launch_f32<128, true>(a, stream) : launch_f32<128, false>(a, stream);
     }
+}
+
+hipError_t launch_prefill_bias(PrefillArgs a, int D, bool causal, int dtype, hipStream_t stream) {
+    // four keys per load when every bias row starts 8-byte aligned
+    const bool vec = (reinterpret_cast<uintptr_t>(a.bias) & 7) == 0 && a.bias_sb % 4 == 0 && a.bias_sh % 4 == 0 &&
+                     a.bias_sq % 4 == 0;
+    if (dtype == kDtypeBF16)
+        return vec ? dispatch_d_bias<bf16_tag, 4>(a, D, causal, stream) : dispatch_d_bias<bf16_tag, 1>(a, D, causal, stream);
+    return vec ? dispatch_d_bias<f16_tag, 4>(a, D, causal, stream) : dispatch_d_bias<f16_tag, 1>(a, D, causal, stream);
 }
 
 }  // namespace gqa

@@ -1,8 +1,8 @@
 /*
  * gqa_attn.h - C ABI of the MI355X (gfx950) GQA attention forward library.
  *
- * Two operations, both the forward pass of softmax attention with grouped
- * query heads:
+ * The forward pass of softmax attention with grouped query heads, prefill and
+ * split-K decode, and the backward of the split-K merge:
  *
  *   attn_fwd            prefill / general forward, FlashAttention style
  *                       (causal_forward_kernel.py, `_flash_attention_forward_gqa_kernel`
@@ -24,6 +24,15 @@
  *                       the same with q_len queries per sequence at its last
  *                       positions, causal among themselves (the IS_CAUSAL /
  *                       NUM_QUERIES_CAUSAL case of `_fwd_kernel_splitK`).
+ *   attn_fwd_bias, attn_decode_splitk_bias
+ *                       prefill / decode with an additive attention bias (the
+ *                       HAS_ADDITIVE_BIAS case of `_fwd_kernel_splitK`).
+ *   attn_splitk_merge_backward
+ *                       gradients of the split-K merge with respect to the
+ *                       partial results (`_splitK_reduce_varargs_backward`).
+ *   attn_decode_splitk_noalloc
+ *                       attn_decode_splitk with the library's own fixed scratch
+ *                       instead of a workspace, for callers that cannot allocate.
  *
  * What is computed, for batch b, query head h, query row i:
  *   g      = h / (Hq / Hkv)                       (query head -> K/V head)
@@ -107,6 +116,34 @@ typedef enum {
 gqa_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                       int B, int Hq, int Hkv, int q_len, int kv_len, int D,
                       float scale, int causal, gqa_dtype_t dtype, void* hip_stream);
+
+/*
+ * attn_fwd_bias - attn_fwd with an additive attention bias: the
+ * HAS_ADDITIVE_BIAS case of splitk_kernels.py (`_fwd_kernel_splitK` loads a
+ * block of a strided bias tensor per tile and adds it to the scaled scores).
+ *
+ *   s_j    = scale * <q[b,h,i,:], k[b,g,j,:]> + bias(b, h, i, j)
+ *   bias(b, h, i, j) = bias[b * bias_stride_b + h * bias_stride_h + i * bias_stride_q + j]
+ *
+ * then the softmax, output and LSE of attn_fwd over the visible keys (the
+ * causal flag still applies).  The bias is in the softmax's natural units (a
+ * bias of log w multiplies a key's weight by w), stored in `dtype` (F16 or
+ * BF16), keys contiguous; strides are in elements, >= 0, and a stride of 0
+ * broadcasts over that dimension (e.g. one [q_len, kv_len] bias for every
+ * batch entry and head).  A bias of -inf masks a key; a row whose visible keys
+ * are all masked gets o = 0, lse = -inf.  +inf or NaN biases are undefined.
+ *
+ *   bias  device memory, read only at (b, h, i, j) with j < kv_len; 2-byte
+ *         aligned (rows that start 8-byte aligned, i.e. all strides multiples
+ *         of 4 and bias 8-byte aligned, are read four keys at a time).
+ *
+ * Other arguments, layouts and results as attn_fwd; dtype F32 returns
+ * GQA_ERR_UNSUPPORTED.  Runs the four-wave kernel.
+ */
+gqa_status_t attn_fwd_bias(const void* q, const void* k, const void* v, const void* bias, long long bias_stride_b,
+                           long long bias_stride_h, long long bias_stride_q, void* o, float* lse, int B, int Hq,
+                           int Hkv, int q_len, int kv_len, int D, float scale, int causal, gqa_dtype_t dtype,
+                           void* hip_stream);
 
 /*
  * attn_fwd_split - the same forward with the keys of every block of query rows
@@ -313,6 +350,34 @@ gqa_status_t attn_decode_splitk_multi(const void* q, const void* k, const void* 
                                       gqa_dtype_t dtype, void* hip_stream);
 
 /*
+ * attn_decode_splitk_bias - attn_decode_splitk_multi with an additive
+ * attention bias: the HAS_ADDITIVE_BIAS case of splitk_kernels.py
+ * (`_fwd_kernel_splitK` adds a strided bias block to the scaled scores).
+ * Query i of sequence b and head h scores key t as
+ *
+ *   s = scale * <q[b,h,i,:], k_t> + bias[b * bias_stride_b + h * bias_stride_h + i * bias_stride_q + t]
+ *
+ * with the visibility, merge and results of attn_decode_splitk_multi (q_len
+ * = 1 is plain decode).  The bias is in the softmax's natural units, stored
+ * in `dtype` (F16 / BF16), keys contiguous; -inf masks a key (a query whose
+ * visible keys are all masked gets o = 0, lse = -inf).
+ *
+ *   bias  device memory, 4-byte aligned; strides in elements, >= 0 and even
+ *         (0 broadcasts).  Keys are read in pairs: every bias row used must be
+ *         readable up to key seq_lens[b] rounded up to an even count (a row
+ *         of an odd length needs one more element, e.g. a padded row stride).
+ *
+ * Other arguments, layouts, errors and the workspace
+ * (attn_decode_workspace_bytes_multi) as for attn_decode_splitk_multi.
+ */
+gqa_status_t attn_decode_splitk_bias(const void* q, const void* k, const void* v, const void* bias,
+                                     long long bias_stride_b, long long bias_stride_h, long long bias_stride_q,
+                                     void* o, float* lse, const int* seq_lens, const int* block_table,
+                                     int max_pages_per_seq, int page_size, int B, int Hq, int Hkv, int q_len, int D,
+                                     int max_kv_len, float scale, int n_splits, void* workspace,
+                                     size_t workspace_bytes, gqa_dtype_t dtype, void* hip_stream);
+
+/*
  * attn_decode_splitk_noalloc - attn_decode_splitk without a workspace argument,
  * for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation).
@@ -341,6 +406,36 @@ gqa_status_t attn_decode_splitk_noalloc(const void* q, const void* k, const void
                                         int max_pages_per_seq, int page_size,
                                         int B, int Hq, int Hkv, int D, int max_kv_len,
                                         float scale, int n_splits, gqa_dtype_t dtype, void* hip_stream);
+
+/*
+ * attn_splitk_merge_backward - gradients of the split-K merge with respect to
+ * the partial results (splitk_kernels.py, `_splitK_reduce_varargs_backward`,
+ * the backward of `_splitK_reduce`).  Per row, the forward merge of n_splits
+ * partials (O_s, L_s) is O = sum_s w_s O_s, L = log sum_s exp(L_s), with
+ * w_s = exp(L_s - L); given (O, L) and the gradients (dO, dL) of some scalar
+ * with respect to them:
+ *
+ *   dO_s = w_s * dO
+ *   dL_s = w_s * (dL + sum_d (O_s[d] - O[d]) * dO[d])
+ *
+ * A partial with L_s = -inf (an empty chunk), and every partial of a row with
+ * L = -inf, gets dO_s = 0, dL_s = 0.
+ *
+ *   o_parts     [rows, n_splits, D] float32   (read; the layout of the decode
+ *   lse_parts   [rows, n_splits]    float32    workspace's partials)
+ *   o, d_o      [rows, D]           float32   (read; merged output and its gradient)
+ *   lse, d_lse  [rows]              float32   (read; natural-log LSE and its gradient)
+ *   d_o_parts   [rows, n_splits, D] float32   (written)
+ *   d_lse_parts [rows, n_splits]    float32   (written)
+ *
+ * All device pointers, 4-byte aligned, owned by the caller; outputs must not
+ * alias inputs.  1 <= n_splits <= 65536, 1 <= D <= 512, 0 <= rows < 2^36.
+ * rows == 0 returns GQA_OK without launching.  Arithmetic in fp32.
+ * Returns GQA_ERR_INVALID_ARG / GQA_ERR_HIP or GQA_OK.
+ */
+gqa_status_t attn_splitk_merge_backward(const float* o_parts, const float* lse_parts, const float* o,
+                                        const float* lse, const float* d_o, const float* d_lse, float* d_o_parts,
+                                        float* d_lse_parts, long long rows, int n_splits, int D, void* hip_stream);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* attn_status_str(gqa_status_t s);

@@ -57,6 +57,33 @@ def test_noalloc_decode_rejects_requests_beyond_its_scratch(L):
     assert L.attn_decode_splitk_noalloc(*p, 4, 256, 128, 32, 8, 128, 1024, 0.088, 16, BF16, None) == WORKSPACE  # 33.8 MB
 
 
+def test_bias_and_merge_backward_validation(L):
+    args = (P[0], P[1], P[2], P[5])
+    # attn_fwd_bias: strides >= 0, a bias pointer, 16-bit dtypes only
+    assert L.attn_fwd_bias(*args, 0, 0, 8, P[3], P[4], 1, 4, 2, 8, 8, 64, 0.125, 1, F32, None) == UNSUPPORTED
+    assert L.attn_fwd_bias(*args, -1, 0, 8, P[3], P[4], 1, 4, 2, 8, 8, 64, 0.125, 1, BF16, None) == INVALID
+    assert L.attn_fwd_bias(P[0], P[1], P[2], None, 0, 0, 8, P[3], P[4], 1, 4, 2, 8, 8, 64, 0.125, 1, BF16,
+                           None) == INVALID
+    assert L.attn_fwd_bias(P[0], P[1], P[2], ctypes.c_void_p(0x10001), 0, 0, 8, P[3], P[4], 1, 4, 2, 8, 8, 64,
+                           0.125, 1, BF16, None) == INVALID          # bias not 2-byte aligned
+    assert L.attn_fwd_bias(*args, 0, 0, 8, P[3], P[4], 0, 4, 2, 8, 8, 64, 0.125, 1, BF16, None) == OK
+    # attn_decode_splitk_bias: even strides, 4-byte aligned bias
+    d = (P[0], P[1], P[2], P[5])
+    rest = (P[3], P[4], P[6], P[7], 4, 16, 2, 8, 2, 1, 64, 64, 0.125, 4, P[7], 1 << 20, BF16, None)
+    assert L.attn_decode_splitk_bias(*d, 0, 0, 7, *rest) == INVALID
+    assert L.attn_decode_splitk_bias(*d, 0, -2, 8, *rest) == INVALID
+    assert L.attn_decode_splitk_bias(P[0], P[1], P[2], ctypes.c_void_p(0x10002), 0, 0, 8, *rest) == INVALID
+    # merge backward: sizes
+    m = [P[i] for i in range(8)]
+    assert L.attn_splitk_merge_backward(*m, 0, 16, 128, None) == OK
+    assert L.attn_splitk_merge_backward(*m, 10, 0, 128, None) == INVALID
+    assert L.attn_splitk_merge_backward(*m, 10, 16, 0, None) == INVALID
+    assert L.attn_splitk_merge_backward(*m, 10, 16, 513, None) == INVALID
+    assert L.attn_splitk_merge_backward(*m, -1, 16, 128, None) == INVALID
+    m[3] = None
+    assert L.attn_splitk_merge_backward(*m, 10, 16, 128, None) == INVALID
+
+
 def test_ceiling_validation(L):
     assert L.gqa_ceiling_mfma_flops(256, 100) == 256 * 8 * 100 * 16 * 32768
     assert L.gqa_ceiling_mfma_flops(0, 100) == 0

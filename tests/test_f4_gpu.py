@@ -1,0 +1,211 @@
+"""GPU parity of the additive bias (prefill and decode) and of the split-K
+merge backward, through the C ABI, against the fp64 oracle (splitk_kernels.py:
+`_fwd_kernel_splitK` HAS_ADDITIVE_BIAS, `_splitK_reduce_varargs_backward`).
+
+Tolerances: bf16 / fp16 attention 2e-2 on O and 1e-3 on LSE (every element);
+the fp32 merge backward |gpu - oracle| <= 1e-5 * (1 + scale of the terms),
+from the fp32 rounding of a D-term dot product and one exponential.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import gqa_attention_forward_attn_amd as gqa
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+gqa.set_check_tables(True)
+
+TOL_O, TOL_L = 2e-2, 1e-3
+DT = {"bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def check(o, l, o_ref, l_ref, what):
+    o = np.asarray(o, dtype=np.float64)
+    l = np.asarray(l, dtype=np.float64)
+    assert not np.isnan(o).any() and not np.isnan(l).any(), f"{what}: NaN"
+    assert np.array_equal(np.isneginf(l), np.isneginf(l_ref)), f"{what}: -inf LSE pattern differs"
+    err_o = np.abs(o - o_ref).max() if o_ref.size else 0.0
+    fin = ~np.isneginf(l_ref)
+    err_l = np.abs(l[fin] - l_ref[fin]).max() if fin.any() else 0.0
+    assert err_o <= TOL_O, f"{what}: max |O - oracle| = {err_o:.3e}"
+    assert err_l <= TOL_L, f"{what}: max |LSE - oracle| = {err_l:.3e}"
+    return err_o, err_l
+
+
+def make_bias(kind, B, Hq, Lq, Lk, dtype, seed, pad=0):
+    """A bias of `kind` on the GPU: a view of a [.., Lk + pad] tensor (pad > 0
+    leaves row starts unaligned for the four-key loads)."""
+    g = torch.Generator().manual_seed(seed)
+    shape = {"full": (B, Hq, Lq, Lk + pad), "per_head": (1, Hq, Lq, Lk + pad), "per_batch": (B, 1, Lq, Lk + pad),
+             "keys_only": (1, 1, 1, Lk + pad)}[kind]
+    full = (2.0 * torch.randn(shape, generator=g)).to(DT[dtype])
+    return full[..., pad:pad + Lk] if pad else full
+
+
+# ---- prefill with a bias ---------------------------------------------------------
+
+PREFILL_BIAS = [
+    # B, Hq, Hkv, q_len, kv_len, D, dtype, causal, bias kind, pad
+    (2, 8, 2, 200, 256, 128, "bf16", True, "full", 0),        # four keys per load
+    (1, 8, 8, 130, 333, 64, "f16", False, "per_head", 0),      # odd key count: key-by-key loads
+    (2, 4, 2, 300, 100, 64, "bf16", True, "per_batch", 0),     # q_len > kv_len: leading rows empty
+    (1, 32, 4, 96, 416, 128, "bf16", True, "keys_only", 0),    # G = 8 with offset, one row for all
+    (1, 6, 3, 257, 257, 128, "f16", True, "full", 1),          # rows unaligned (a view one key in)
+    (3, 4, 4, 65, 1, 64, "bf16", False, "full", 0),            # one key
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_BIAS, ids=lambda c: "-".join(map(str, c)))
+def test_prefill_bias_all_elements(case):
+    B, Hq, Hkv, Lq, Lk, D, dt, causal, kind, pad = case
+    print(f"prefill bias {case}", flush=True)
+    q, k, v = W.make_prefill(B, Hq, Hkv, Lq, Lk, D, dt, seed=sum(case[:6]))
+    bias = make_bias(kind, B, Hq, Lq, Lk, dt, seed=Lq + Lk, pad=pad)
+    scale = W.fp32_scale(D)
+    out = torch.full((B, Hq, Lq, D), float("nan"), dtype=q.dtype, device="cuda")
+    lse = torch.full((B, Hq, Lq), float("nan"), dtype=torch.float32, device="cuda")
+    o, l = gqa.attn_fwd_bias(q.cuda(), k.cuda(), v.cuda(), bias.cuda(), causal=causal, scale=scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attn_fwd_bias(q, k, v, bias, scale, causal)
+    check(o.double().cpu().numpy(), l.double().cpu().numpy(), o_ref, l_ref, str(case))
+
+
+def test_prefill_zero_bias_is_the_plain_kernel_bitwise():
+    q, k, v = W.make_prefill(2, 8, 2, 200, 300, 128, "bf16", seed=1)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    zero = torch.zeros(1, 1, 1, 300, dtype=torch.bfloat16, device="cuda")
+    for causal in (True, False):
+        o1, l1 = gqa.attn_fwd(qd, kd, vd, causal=causal, scale=0.09, kernel="fourwave")
+        o2, l2 = gqa.attn_fwd_bias(qd, kd, vd, zero, causal=causal, scale=0.09)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_prefill_causal_as_minus_inf_bias_and_masked_rows():
+    # the bottom-right pattern as a -inf bias without the causal flag gives the
+    # causal result bitwise; a row masked entirely gives (0, -inf)
+    Lq, Lk = 150, 333
+    q, k, v = W.make_prefill(1, 8, 2, Lq, Lk, 64, "f16", seed=2)
+    i = torch.arange(Lq).view(-1, 1)
+    j = torch.arange(Lk).view(1, -1)
+    bias = torch.where(j <= i + (Lk - Lq), 0.0, float("-inf")).to(torch.float16).view(1, 1, Lq, Lk)
+    bias = bias.expand(1, 8, Lq, Lk).contiguous()
+    bias[0, 3, 7, :] = float("-inf")
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    o1, l1 = gqa.attn_fwd(qd, kd, vd, causal=True, scale=0.125, kernel="fourwave")
+    o2, l2 = gqa.attn_fwd_bias(qd, kd, vd, bias.cuda(), causal=False, scale=0.125)
+    o1, l1, o2, l2 = o1.cpu(), l1.cpu(), o2.cpu(), l2.cpu()
+    keep = torch.ones(1, 8, Lq, dtype=torch.bool)
+    keep[0, 3, 7] = False
+    assert torch.equal(o1[keep], o2[keep]) and torch.equal(l1[keep], l2[keep])
+    assert torch.all(o2[0, 3, 7] == 0) and torch.isneginf(l2[0, 3, 7])
+
+
+def test_prefill_bias_headline_shape_per_head_bias():
+    # the causal GQA prefill workload (B=2, Hq=32, Hkv=8, S=2048, D=128) with one
+    # [S, S] bias per head shared by the batch (stride 0): every element
+    spec = W.CAUSAL_GQA_PREFILL
+    print("prefill bias at the headline shape", flush=True)
+    q, k, v = W.make_prefill_spec(spec)
+    bias = make_bias("per_head", spec.B, spec.Hq, spec.q_len, spec.kv_len, "bf16", seed=2048)
+    scale = W.fp32_scale(spec.D)
+    o, l = gqa.attn_fwd_bias(q.cuda(), k.cuda(), v.cuda(), bias.cuda(), causal=True, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attn_fwd_bias(q, k, v, bias, scale, True)
+    e_o, e_l = check(o.double().cpu().numpy(), l.double().cpu().numpy(), o_ref, l_ref, "headline + bias")
+    print(f"headline + per-head bias: max|dO|={e_o:.3e} max|dLSE|={e_l:.3e}")
+
+
+# ---- decode with a bias -----------------------------------------------------------
+
+def gpu_decode_bias(inp, bias, n_splits, scale, q4):
+    out = torch.full(q4.shape, float("nan"), dtype=q4.dtype, device="cuda")
+    lse = torch.full(q4.shape[:3], float("nan"), dtype=torch.float32, device="cuda")
+    o, l = gqa.attn_decode_splitk_bias(q4.cuda(), inp.k_cache.cuda(), inp.v_cache.cuda(), inp.seq_lens.cuda(),
+                                       bias.cuda(), block_table=inp.block_table.cuda(), n_splits=n_splits,
+                                       scale=scale, max_kv_len=inp.max_kv_len, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return o.double().cpu().numpy(), l.double().cpu().numpy()
+
+
+DECODE_BIAS = [
+    # B, Hq, Hkv, D, dtype, q_len, page_size, lens (lo, hi), n_splits, bias kind
+    (16, 32, 8, 128, "bf16", 1, 256, (1024, 32768), 16, "full"),     # the paged decode workload's shape
+    (4, 8, 2, 64, "f16", 1, 16, (1, 700), 5, "per_head"),
+    (3, 32, 4, 128, "bf16", 4, 64, (3, 900), 7, "full"),             # multi-query, some sequences < q_len
+    (5, 16, 16, 64, "bf16", 2, 1, (1, 300), 3, "per_batch"),        # G = 1, pages of one token
+]
+
+
+@pytest.mark.parametrize("case", DECODE_BIAS, ids=lambda c: "-".join(map(str, c)))
+def test_decode_bias_all_rows(case):
+    B, Hq, Hkv, D, dt, q_len, ps, (lo, hi), S, kind = case
+    print(f"decode bias {case}", flush=True)
+    inp = W.make_decode(B, Hq, Hkv, D, dt, seed=B * Hq + q_len, len_lo=lo, len_hi=hi, page_size=ps,
+                        q_len=q_len if q_len > 1 else None)
+    q4 = inp.q if inp.q.dim() == 4 else inp.q.unsqueeze(2)
+    L = int(inp.seq_lens.max())
+    L += L % 2  # rows of an even key count: odd sequences read one padding key
+    bias = make_bias(kind, B, Hq, q_len, L, dt, seed=L)
+    if kind == "full":
+        bias[0, 1, 0, :5] = float("-inf")   # a few masked keys
+        bias[1, 0, :, :] = float("-inf")    # a head masked entirely: (0, -inf)
+    scale = W.fp32_scale(D)
+    o, l = gpu_decode_bias(inp, bias, S, scale, q4)
+    o_ref, l_ref = oracle.attn_decode_bias(q4, inp.k_cache, inp.v_cache, inp.seq_lens, bias, scale,
+                                           block_table=inp.block_table, max_kv_len=inp.max_kv_len)
+    e_o, e_l = check(o, l, o_ref, l_ref, str(case))
+    print(f"decode bias {case}: max|dO|={e_o:.3e} max|dLSE|={e_l:.3e}")
+
+
+def test_decode_zero_bias_is_plain_decode_bitwise():
+    inp = W.make_decode(4, 16, 4, 128, "bf16", seed=9, len_lo=100, len_hi=2000, page_size=32)
+    L = int(inp.seq_lens.max()) + 1
+    L += L % 2
+    zero = torch.zeros(1, 1, 1, L, dtype=torch.bfloat16)
+    o1, l1 = gpu_decode_bias(inp, zero, 8, 0.088, inp.q.unsqueeze(2))
+    qd = inp.q.cuda()
+    o2, l2 = gqa.attn_decode_splitk(qd, inp.k_cache.cuda(), inp.v_cache.cuda(), inp.seq_lens.cuda(),
+                                    block_table=inp.block_table.cuda(), n_splits=8, scale=0.088,
+                                    max_kv_len=inp.max_kv_len)
+    assert np.array_equal(o1[:, :, 0], o2.double().cpu().numpy())
+    assert np.array_equal(l1[:, :, 0], l2.double().cpu().numpy())
+
+
+# ---- merge backward -----------------------------------------------------------------
+
+def _merge_inputs(rows, S, D, seed, n_empty):
+    g = np.random.default_rng(seed)
+    op = g.standard_normal((rows, S, D)).astype(np.float32)
+    lp = (3.0 * g.standard_normal((rows, S))).astype(np.float32)
+    for r, s in zip(g.integers(0, rows, n_empty), g.integers(0, S, n_empty)):
+        op[r, s] = 0.0
+        lp[r, s] = -np.inf
+    lp[0, :] = -np.inf                       # a row with no key at all
+    op[0] = 0.0
+    o, lse = oracle.splitk_merge(op, lp)     # merged forward in fp64, handed over in fp32
+    o, lse = o.astype(np.float32), lse.astype(np.float32)
+    d_o = g.standard_normal((rows, D)).astype(np.float32)
+    d_lse = g.standard_normal(rows).astype(np.float32)
+    return op, lp, o, lse, d_o, d_lse
+
+
+@pytest.mark.parametrize("rows,S,D", [(2048, 16, 128), (300, 1, 64), (77, 5, 96), (512, 64, 128), (9, 3, 512)])
+def test_merge_backward_matches_oracle(rows, S, D):
+    print(f"merge backward rows={rows} S={S} D={D}", flush=True)
+    op, lp, o, lse, d_o, d_lse = _merge_inputs(rows, S, D, seed=rows + S + D, n_empty=rows // 3)
+    dev = [torch.from_numpy(x).cuda() for x in (op, lp, o, lse, d_o, d_lse)]
+    dop, dlp = gqa.attn_splitk_merge_backward(*dev)
+    torch.cuda.synchronize()
+    dop, dlp = dop.double().cpu().numpy(), dlp.double().cpu().numpy()
+    ref_op, ref_lp = oracle.splitk_merge_backward(op, lp, o, lse, d_o, d_lse)
+    assert np.isfinite(dop).all() and np.isfinite(dlp).all()
+    np.testing.assert_array_less(np.abs(dop - ref_op), 1e-5 * (1 + np.abs(ref_op)))
+    with np.errstate(invalid="ignore"):  # -inf - (-inf) on empty rows, replaced by 0
+        w = np.where(np.isneginf(lp) | np.isneginf(lse)[:, None], 0.0,
+                     np.exp(lp.astype(np.float64) - lse.astype(np.float64)[:, None]))
+    terms = w * (np.abs(d_lse)[:, None] + (np.abs(op - o[:, None, :]) * np.abs(d_o)[:, None, :]).sum(-1))
+    np.testing.assert_array_less(np.abs(dlp - ref_lp), 1e-5 * (1 + terms))
+    assert np.all(dop[0] == 0) and np.all(dlp[0] == 0)
