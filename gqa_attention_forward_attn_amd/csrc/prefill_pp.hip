@@ -94,6 +94,15 @@ __device__ __forceinline__ int swz(int r) {
     return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
 }
 
+// 16 bytes per lane into LDS from a wave-uniform base address (SGPRs) plus a
+// 32-bit per-lane byte offset: no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_base) {
+    __asm__ __volatile__("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                         :
+                         : "v"(voff), "s"(sbase), "s"(lds_base)
+                         : "m0");
+}
+
 // 4 bytes per lane from global memory into LDS (lane i -> lds_base + 4 i).
 __device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
     __asm__ __volatile__("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
@@ -132,8 +141,8 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);             // ping-pong group: 0 leads, 1 trails by one phase
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;             // ping-pong group: 0 leads, 1 trails by one phase
     const int half = lane >> 5;
     const int l32 = lane & 31;
 
@@ -242,12 +251,14 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
     const int page_mask = PAGED ? (1 << a.page_shift) - 1 : 0;
     const size_t tok_bytes = PAGED ? (size_t)a.Hkv * ROWB : (size_t)ROWB;  // bytes between key rows
     int ld_row[LPW], ld_col[LPW];
+    [[maybe_unused]] uint32_t ld_voff[LPW];  // byte offset of the lane's chunk in a dense tile
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
         const int p = (wave * LPW + j) * 64 + lane;  // chunk position in the tile
         const int row = p / CPR, pc = p % CPR;
         ld_row[j] = row;
         ld_col[j] = (pc ^ swz<D>(row)) * 16;
+        ld_voff[j] = (uint32_t)(row * ROWB + ld_col[j]);
     }
     // PAGED: this wave's page-id ring; lane i of the load for tile t fetches the
     // page of key row i
@@ -262,6 +273,18 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
     auto issue_tile = [&](int t) {
         const int t0 = (t_lo + t) * BN;
         lds_char* st = smem + (t % NST) * STAGEB;
+        if (!PAGED && t0 + BN <= kv_len) {
+            // a whole dense tile: one uniform base per tile, constant lane offsets
+            const char* kb = kg + (size_t)t0 * ROWB;
+            const char* vb = vg + (size_t)t0 * ROWB;
+#pragma unroll
+            for (int j = 0; j < LPW; ++j) {
+                const uint32_t dst = (uint32_t)(uintptr_t)(st + (wave * LPW + j) * 1024);
+                dma16(kb, ld_voff[j], dst);
+                dma16(vb, ld_voff[j], dst + TILEB);
+            }
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < LPW; ++j) {
             const int key = min(t0 + ld_row[j], last_key);
