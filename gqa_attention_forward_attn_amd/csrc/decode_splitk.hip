@@ -197,7 +197,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
     constexpr int PER_SLICE = 2 * NI + (BIAS ? 2 : 0);
     static_assert((NST - 1) * PER_SLICE < 64, "vmcnt range");
     static_assert((NST & (NST - 1)) == 0, "NST must be a power of two");
-    static_assert(NW * 16 * (D + 3) * 4 <= NW * WAVEB, "merge buffers must fit in the ring");
+    static_assert((NW * 16 * (D + 4) + 3 * NW * 16) * 4 <= NW * WAVEB, "merge buffers must fit in the ring");
 
     __shared__ __attribute__((aligned(1024))) char smem_raw[NW * WAVEB];
     lds_char* smem = (lds_char*)smem_raw;
@@ -410,18 +410,26 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
     }
 
     // ---- merge the NW waves' partial results -------------------------------
+    // Every wave's acc goes to LDS (rows padded by 16 bytes, so that the four
+    // rows of one store instruction fall into distinct banks); the merged rows
+    // are written as 16-byte pieces.  The partial rows are what a workgroup
+    // writes last, and with one workgroup per CU the next one starts only when
+    // they are out, so their cost grows with the columns of the block (16
+    // query rows cost 8 KB per workgroup against 2 KB for one query of four
+    // heads).
     l += shfl_xor(l, 16);
     l += xor32(l);
     __syncthreads();  // every wave is done with its ring (and its loads have landed)
-    float* sacc = reinterpret_cast<float*>(smem_raw);  // [NW][16][D]
-    float* sm = sacc + NW * 16 * D;                    // [NW][16]
+    constexpr int SROW = D + 4;                        // floats per padded row
+    float* sacc = reinterpret_cast<float*>(smem_raw);  // [NW][16][SROW]
+    float* sm = sacc + NW * 16 * SROW;                 // [NW][16]
     float* sl = sm + NW * 16;                          // [NW][16]
     {
         const int kq = lane >> 4, c = lane & 15;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sacc[(wave * 16 + 4 * kq + r) * D + 16 * nb + c] = acc[nb][r];
+            for (int r = 0; r < 4; ++r) sacc[(wave * 16 + 4 * kq + r) * SROW + 16 * nb + c] = acc[nb][r];
         if (lane < 16) {
             sm[wave * 16 + lane] = m;
             sl[wave * 16 + lane] = l;
@@ -451,12 +459,19 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
         a.part_lse[prow + (size_t)h * a.n_splits] = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
     }
     __syncthreads();
-    for (int i = tid; i < nh * D; i += NW * 64) {
-        const int h = i / D, d = i % D;
-        float O = 0.f;
+    constexpr int V4 = D / 4;  // 16-byte pieces per row
+    for (int i = tid; i < nh * V4; i += NW * 64) {
+        const int h = i / V4, d = 4 * (i % V4);
+        f32x4 O = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int w = 0; w < NW; ++w) O = fmaf(se[w * 16 + h], sacc[(w * 16 + h) * D + d], O);
-        a.part_o[(prow + (size_t)h * a.n_splits) * D + d] = O;
+        for (int w = 0; w < NW; ++w) {
+            const float e = se[w * 16 + h];
+            const f32x4 x = *reinterpret_cast<const f32x4*>(sacc + (w * 16 + h) * SROW + d);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) O[k] = fmaf(e, x[k], O[k]);
+        }
+        // streamed past L2: the combine kernel reads them once, after every chunk
+        __builtin_nontemporal_store(O, reinterpret_cast<f32x4*>(a.part_o + (prow + (size_t)h * a.n_splits) * D + d));
     }
 }
 
@@ -531,7 +546,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel_fp8(DecodeArgs
     static_assert(PG != kPagedSmall, "E4M3 pages hold at least one 16-token slice");
     static_assert((NST - 1) * PER_SLICE < 64, "vmcnt range");
     static_assert((NST & (NST - 1)) == 0, "NST must be a power of two");
-    static_assert(NW * 16 * (D + 3) * 4 <= NW * WAVEB, "merge buffers must fit in the ring");
+    static_assert((NW * 16 * (D + 4) + 4 * NW * 16) * 4 <= NW * WAVEB, "merge buffers must fit in the ring");
 
     __shared__ __attribute__((aligned(1024))) char smem_raw[NW * WAVEB];
     lds_char* smem = (lds_char*)smem_raw;
@@ -743,8 +758,9 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel_fp8(DecodeArgs
     pb += shfl_xor(pb, 16);
     pb += xor32(pb);
     __syncthreads();  // every wave is done with its ring (and its loads have landed)
-    float* sacc = reinterpret_cast<float*>(smem_raw);  // [NW][16][D]
-    float* sm = sacc + NW * 16 * D;                    // [NW][16]
+    constexpr int SROW = D + 4;                        // floats per padded row
+    float* sacc = reinterpret_cast<float*>(smem_raw);  // [NW][16][SROW]
+    float* sm = sacc + NW * 16 * SROW;                 // [NW][16]
     float* sl = sm + NW * 16;                          // [NW][16]
     float* sp = sl + NW * 16;                          // [NW][16]
     {
@@ -752,7 +768,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel_fp8(DecodeArgs
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sacc[(wave * 16 + 4 * kq + r) * D + 16 * nb + c] = acc[nb][r];
+            for (int r = 0; r < 4; ++r) sacc[(wave * 16 + 4 * kq + r) * SROW + 16 * nb + c] = acc[nb][r];
         if (lane < 16) {
             sm[wave * 16 + lane] = m;
             sl[wave * 16 + lane] = l;
@@ -761,22 +777,40 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel_fp8(DecodeArgs
     }
     __syncthreads();
     const size_t prow = qrow0 * a.n_splits + s;  // partial row of the block's first head
-    for (int i = tid; i < nh * D; i += NW * 64) {
-        const int h = i / D, d = i % D;
+    // per head: the waves' weights relative to the largest running max,
+    // divided by the head's sum, and its LSE
+    float* se = sp + NW * 16;  // [NW][16]
+    if (tid < nh) {
+        const int h = tid;
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < NW; ++w) M = fmaxf(M, sm[w * 16 + h]);
-        float L = 0.f, O = 0.f;
+        float e[NW], L = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
             const float mw = sm[w * 16 + h];
-            const float e = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
-            L += e * sl[w * 16 + h];
-            O += e * (sacc[(w * 16 + h) * D + d] + sp[w * 16 + h]);
+            e[w] = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
+            L += e[w] * sl[w * 16 + h];
         }
-        const size_t row = prow + (size_t)h * a.n_splits;
-        a.part_o[row * D + d] = L > 0.f ? O / L : 0.f;
-        if (d == 0) a.part_lse[row] = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) se[w * 16 + h] = e[w] * inv;
+        a.part_lse[prow + (size_t)h * a.n_splits] = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
+    }
+    __syncthreads();
+    constexpr int V4 = D / 4;  // 16-byte pieces per row
+    for (int i = tid; i < nh * V4; i += NW * 64) {
+        const int h = i / V4, d = 4 * (i % V4);
+        f32x4 O = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float e = se[w * 16 + h];
+            const float shift = sp[w * 16 + h];
+            const f32x4 x = *reinterpret_cast<const f32x4*>(sacc + (w * 16 + h) * SROW + d);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) O[k] = fmaf(e, x[k] + shift, O[k]);
+        }
+        __builtin_nontemporal_store(O, reinterpret_cast<f32x4*>(a.part_o + (prow + (size_t)h * a.n_splits) * D + d));
     }
 }
 
