@@ -23,6 +23,7 @@ struct PrefillArgs {
     int delta;        // kv_len - q_len (bottom-right causal offset)
     int n_pos_tiles;  // filled by the launcher
     int n_rest;       // filled by the launcher
+    int xcd_order;    // ping-pong kernel, dense: XCD-aware work order (filled by the launcher)
     float c;          // scale * log2(e)
     // Split-KV prefill (ping-pong kernel): the key tiles of every row block are
     // cut into kv_splits ranges; range s writes O_s (fp32) and its natural-base

@@ -173,8 +173,22 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
         if (b < 0) return;  // workgroup-uniform, before any barrier: no item left
         from_end = true;
     } else {
-        pt = id / a.n_rest;
-        int rest = id - pt * a.n_rest;
+        int rest;
+        if (!PAGED && a.xcd_order) {
+            // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs
+            // (blockIdx % 8) and XCD x takes the x-th eighth of the items in
+            // (head block, position tile) order, so the workgroups one XCD runs
+            // at a time share a few heads' K/V in its L2 instead of streaming
+            // every head it hosts once per round of position tiles
+            int item = id;
+            const int q8 = a.n_pos_tiles * a.n_rest / 8;
+            if (item < 8 * q8) item = (item % 8) * q8 + item / 8;
+            pt = item % a.n_pos_tiles;
+            rest = item / a.n_pos_tiles;
+        } else {
+            pt = id / a.n_rest;
+            rest = id - pt * a.n_rest;
+        }
         if (CAUSAL) pt = a.n_pos_tiles - 1 - pt;  // longest rows first
         hg = rest % hgroups;
         rest /= hgroups;
@@ -620,6 +634,12 @@ hipError_t launch_pp(PrefillArgs a, hipStream_t stream) {
     a.n_rest = a.B * a.Hkv * (a.group / NH);
     const long long blocks = (long long)a.n_pos_tiles * a.n_rest * (a.kv_splits > 1 ? a.kv_splits : 1);
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    // The plain order runs every position tile of a round next to the other
+    // heads an XCD hosts, ceil(n_rest / 8) of them: when their K and V outgrow
+    // about half of an XCD's 4 MB L2, each round of position tiles reads them
+    // from HBM again, and the XCD-aware order keeps them resident instead.
+    const long long kv_bytes_head = (long long)a.kv_len * D * 4;  // 16-bit K and V of one (b, kv head)
+    a.xcd_order = !PAGED && a.kv_splits <= 1 && a.n_rest >= 8 && (a.n_rest + 7) / 8 * kv_bytes_head > (2LL << 20);
     hipLaunchKernelGGL((prefill_fwd_pp<TAG, D, CAUSAL, NH, PAGED>), dim3((unsigned)blocks), dim3(512), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.kv_splits <= 1) return e;
