@@ -7,7 +7,9 @@ visible (query, key) pairs only (4*D flop per pair; masked work is not
 credited).  The other workloads (fp32 correctness shape, bottom-right offset
 prefill, non-causal fp16 MHA, split-K paged decode over a 16-bit and over an
 E4M3 cache, decode with four queries per sequence, ragged prefill over a paged
-cache) are timed the same way and reported under "workloads".
+cache, the headline prefill and the paged decode with an additive bias, the
+backward of the split-K merge) are timed the same way and reported under
+"workloads".
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--only NAME]
 """
@@ -187,6 +189,119 @@ def bench_decode_fp8(spec, steps, warmup):
     }
 
 
+def bench_prefill_bias(spec, steps, warmup):
+    """attn_fwd_bias on the headline shape with a per-head bias [1, Hq, q_len,
+    kv_len] (the four-wave kernel's bias form)."""
+    q, k, v, bias = W.make_prefill_bias_spec(spec)
+    dev = torch.device("cuda:0")
+    q, k, v, bias = q.to(dev), k.to(dev), v.to(dev), bias.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    scale = W.fp32_scale(spec.D)
+
+    def step():
+        gqa.attn_fwd_bias(q, k, v, bias, causal=spec.causal, scale=scale, out=o, lse=lse)
+
+    wall, kern_s, per = time_launches(step, steps, warmup)
+    flops = prefill_flops(spec)
+    return {
+        "workload": spec.name, "dtype": spec.dtype, "causal": spec.causal,
+        "shape": {"B": spec.B, "Hq": spec.Hq, "Hkv": spec.Hkv, "q_len": spec.q_len,
+                  "kv_len": spec.kv_len, "D": spec.D, "bias": [1, spec.Hq, spec.q_len, spec.kv_len]},
+        "kernel": "prefill_fwd_mfma<bf16, D=128, causal, bias>",
+        "flop_per_launch": flops,
+        "bias_bytes": bias.numel() * bias.element_size(),
+        "ms_per_step": wall / steps * 1e3,
+        "kernel_ms_mean": kern_s * 1e3, "call_span_ms_min": float(per.min()) * 1e3,
+        "tflops": flops * steps / wall / 1e12,
+        "kernel_tflops": flops / kern_s / 1e12,
+        "peak_tflops": PEAK_MFMA_16BIT_TFLOPS,
+        "frac_of_peak": flops / kern_s / 1e12 / PEAK_MFMA_16BIT_TFLOPS,
+    }
+
+
+def decode_bias_bytes(spec, inp) -> int:
+    """Bias bytes a decode step needs: one 16-bit value per (sequence, head,
+    query, key)."""
+    return int(inp.seq_lens.to(torch.int64).sum()) * spec.Hq * spec.q_len * 2
+
+
+def bench_decode_bias(spec, steps, warmup):
+    """attn_decode_splitk_bias on the paged decode shape with a bias per
+    (sequence, head) over its keys."""
+    inp, bias = W.make_decode_bias_spec(spec)
+    dev = torch.device("cuda:0")
+    q = inp.q.to(dev).reshape(spec.B, spec.Hq, spec.q_len, spec.D)
+    kc, vc = inp.k_cache.to(dev), inp.v_cache.to(dev)
+    sl, bt, bias = inp.seq_lens.to(dev), inp.block_table.to(dev), bias.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+    ws = torch.empty(gqa.decode_workspace_bytes_multi(spec.B, spec.Hq, spec.q_len, spec.D, spec.n_splits),
+                     dtype=torch.uint8, device=dev)
+    scale = W.fp32_scale(spec.D)
+
+    def step():
+        gqa.attn_decode_splitk_bias(q, kc, vc, sl, bias, block_table=bt, n_splits=spec.n_splits, scale=scale,
+                                    max_kv_len=inp.max_kv_len, workspace=ws, out=o, lse=lse)
+
+    wall, kern_s, per = time_launches(step, steps, warmup)
+    nbytes = decode_bytes(spec, inp) + decode_bias_bytes(spec, inp)
+    return {
+        "workload": spec.name, "dtype": spec.dtype,
+        "shape": {"B": spec.B, "Hq": spec.Hq, "Hkv": spec.Hkv, "D": spec.D, "q_len": spec.q_len,
+                  "page_size": spec.page_size, "n_splits": spec.n_splits,
+                  "sum_kv_len": int(inp.seq_lens.to(torch.int64).sum()),
+                  "bias": [spec.B, spec.Hq, spec.q_len, inp.max_kv_len]},
+        "bytes_per_step": nbytes,
+        "bias_bytes": decode_bias_bytes(spec, inp),
+        "ms_per_step": wall / steps * 1e3,
+        "kernel_ms_mean": kern_s * 1e3, "call_span_ms_min": float(per.min()) * 1e3,
+        "gbps": nbytes * steps / wall / 1e9,
+        "kernel_gbps": nbytes / kern_s / 1e9,
+        "peak_gbps": PEAK_HBM_GBPS,
+        "frac_of_peak": nbytes / kern_s / 1e9 / PEAK_HBM_GBPS,
+    }
+
+
+def merge_backward_bytes(spec) -> int:
+    """Bytes of one merge backward: read o_parts, lse_parts, o, lse, d_o, d_lse;
+    write d_o_parts and d_lse_parts (fp32)."""
+    S, D = spec.n_splits, spec.D
+    return spec.rows * 4 * (2 * S * D + 2 * S + 2 * D + 2)
+
+
+def bench_merge_backward(spec, steps, warmup):
+    """attn_splitk_merge_backward over the partials of a split-KV prefill.  The
+    merged (o, lse) it takes are formed from the partials with torch before the
+    timed region (inputs of the backward, not part of what is timed)."""
+    dev = torch.device("cuda:0")
+    op, lp, d_o, d_lse = (t.to(dev) for t in W.make_merge_backward_spec(spec))
+    lse = torch.logsumexp(lp.double(), dim=-1)
+    w = torch.where(torch.isfinite(lse)[:, None], torch.exp(lp.double() - lse[:, None]), torch.zeros_like(lp.double()))
+    o = (w[..., None] * op.double()).sum(dim=-2).float()
+    lse = lse.float()
+    dop = torch.empty_like(op)
+    dlp = torch.empty_like(lp)
+
+    def step():
+        gqa.attn_splitk_merge_backward(op, lp, o, lse, d_o, d_lse, d_o_parts=dop, d_lse_parts=dlp)
+
+    wall, kern_s, per = time_launches(step, steps, warmup)
+    nbytes = merge_backward_bytes(spec)
+    return {
+        "workload": spec.name, "dtype": "f32",
+        "shape": {"rows": spec.rows, "n_splits": spec.n_splits, "D": spec.D},
+        "kernel": "merge_backward_kernel (one wave per row)",
+        "bytes_per_step": nbytes,
+        "ms_per_step": wall / steps * 1e3,
+        "kernel_ms_mean": kern_s * 1e3, "call_span_ms_min": float(per.min()) * 1e3,
+        "gbps": nbytes * steps / wall / 1e9,
+        "kernel_gbps": nbytes / kern_s / 1e9,
+        "peak_gbps": PEAK_HBM_GBPS,
+        "frac_of_peak": nbytes / kern_s / 1e9 / PEAK_HBM_GBPS,
+    }
+
+
 def bench_paged_prefill(spec, steps, warmup):
     inp = W.make_paged_prefill_spec(spec)
     dev = torch.device("cuda:0")
@@ -294,8 +409,55 @@ def cpu_baseline(spec, target_s=12.0):
     GB/s on the step's algorithmic bytes, prorated by the keys each sampled
     row reads (decode)."""
     import oracle
+    if isinstance(spec, W.MergeBwdSpec):
+        op, lp, d_o, d_lse = (t.numpy() for t in W.make_merge_backward_spec(spec))
+        row_bytes = merge_backward_bytes(spec) / spec.rows
+
+        def timed(rows):   # the backward alone; its merged inputs are formed first, untimed
+            o_l = oracle.splitk_merge(op[rows], lp[rows])
+            t0 = time.perf_counter()
+            oracle.splitk_merge_backward(op[rows], lp[rows], o_l[0], o_l[1], d_o[rows], d_lse[rows])
+            return time.perf_counter() - t0
+
+        rows = _evenly(spec.rows, 2048)
+        dt = timed(rows)
+        rows = _evenly(spec.rows, int(2048 * target_s / max(dt, 1e-3)))
+        dt = timed(rows)
+        n, total = len(rows), spec.rows
+        value, unit = row_bytes * n / dt / 1e9, "GB/s"
+        return {
+            "value": value, "unit": unit, "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n} of {total} rows of {spec.name} (evenly spaced), fp64, {dt:.1f} s on "
+                      f"{oracle.num_threads()} OpenMP threads ({platform.processor() or 'host CPU'})",
+        }
     scale = W.fp32_scale(spec.D)
-    if isinstance(spec, W.DecodeSpec) or spec is W.FP8_PAGED_DECODE:
+    if spec is W.BIAS_PAGED_DECODE:
+        inp, bias = W.make_decode_bias_spec(spec)
+        q4 = inp.q.reshape(spec.B, spec.Hq, spec.q_len, spec.D)
+        total = spec.B * spec.Hq * spec.q_len
+        lens = inp.seq_lens.to(torch.int64).numpy()
+        row_len = lens[np.arange(total) // (spec.Hq * spec.q_len)]
+        step_bytes = decode_bytes(spec, inp) + decode_bias_bytes(spec, inp)
+
+        def run_rows(rows):
+            oracle.attn_decode_bias(q4, inp.k_cache, inp.v_cache, inp.seq_lens, bias, scale,
+                                    block_table=inp.block_table, max_kv_len=inp.max_kv_len, rows=rows)
+
+        work, dt, n = _time_oracle(run_rows, total, lambda r: step_bytes * row_len[r].sum() / row_len.sum(),
+                                   target_s)
+        value, unit = work / dt / 1e9, "GB/s"
+    elif spec is W.BIAS_CAUSAL_GQA_PREFILL:
+        q, k, v, bias = W.make_prefill_bias_spec(spec)
+        total = spec.B * spec.Hq * spec.q_len
+        pos = np.arange(total) % spec.q_len
+        delta = spec.kv_len - spec.q_len
+        vis = np.minimum(spec.kv_len, np.maximum(0, pos + 1 + delta)) if spec.causal else \
+            np.full_like(pos, spec.kv_len)
+        row_flops = 4 * spec.D * vis
+        work, dt, n = _time_oracle(lambda r: oracle.attn_fwd_bias(q, k, v, bias, scale, spec.causal, rows=r),
+                                   total, lambda r: row_flops[r].sum(), target_s)
+        value, unit = work / dt / 1e12, "TFLOP/s"
+    elif isinstance(spec, W.DecodeSpec) or spec is W.FP8_PAGED_DECODE:
         fp8 = spec is W.FP8_PAGED_DECODE
         inp = W.make_decode_fp8_spec(spec) if fp8 else W.make_decode_spec(spec)
         q_len = 1 if fp8 else spec.q_len
@@ -390,6 +552,12 @@ def bench_read_ceiling(steps, warmup):
 
 
 def run_one(spec, steps, warmup):
+    if spec is W.BIAS_CAUSAL_GQA_PREFILL:
+        return bench_prefill_bias(spec, steps, warmup)
+    if spec is W.BIAS_PAGED_DECODE:
+        return bench_decode_bias(spec, steps, warmup)
+    if isinstance(spec, W.MergeBwdSpec):
+        return bench_merge_backward(spec, steps, warmup)
     if spec is W.FP8_PAGED_DECODE:
         return bench_decode_fp8(spec, steps, warmup)
     if isinstance(spec, W.DecodeSpec):
@@ -420,7 +588,8 @@ def main():
 
     all_specs = [W.CAUSAL_GQA_FP32, W.CAUSAL_GQA_PREFILL, W.CAUSAL_GQA_OFFSET,
                  W.MHA_NONCAUSAL_FP16, W.PAGED_DECODE, W.FP8_PAGED_DECODE, W.MULTI_QUERY_DECODE,
-                 W.RAGGED_PAGED_PREFILL]
+                 W.RAGGED_PAGED_PREFILL, W.BIAS_CAUSAL_GQA_PREFILL, W.BIAS_PAGED_DECODE,
+                 W.SPLITK_MERGE_BACKWARD]
     ceilings = {"mfma_ceiling": bench_mfma_ceiling, "hbm_read_ceiling": bench_read_ceiling}
     if args.only == "hbm_copy":
         print(json.dumps(bench_copy(args.steps, args.warmup)), flush=True)

@@ -274,3 +274,66 @@ def make_decode_fp8(B, Hq, Hkv, D, dtype="bf16", seed=0, len_lo=1, len_hi=64, pa
 def make_decode_fp8_spec(spec: DecodeSpec):
     return make_decode_fp8(spec.B, spec.Hq, spec.Hkv, spec.D, spec.dtype, spec.seed, spec.len_lo, spec.len_hi,
                            spec.page_size, spec.max_pages)
+
+
+# ---- additive bias and split-K merge backward ------------------------------------
+
+# The headline prefill shape with a per-head additive bias [1, Hq, q_len, kv_len]
+# (shared by the batch, like a relative-position bias), and the paged decode
+# shape with a bias per (sequence, head) over its keys [B, Hq, 1, max_kv_len]
+# (the HAS_ADDITIVE_BIAS operand of the split-K decode page).
+BIAS_CAUSAL_GQA_PREFILL = PrefillSpec("bias_causal_gqa_prefill", 2, 32, 8, 2048, 2048, 128, "bf16", True, 20270)
+BIAS_PAGED_DECODE = DecodeSpec("bias_paged_decode", 16, 32, 8, 128, "bf16", 1024, 32768, 256, 128, 16, 20271)
+
+
+@dataclass(frozen=True)
+class MergeBwdSpec:
+    name: str
+    rows: int            # merged rows (query, head)
+    n_splits: int
+    D: int
+    empty: int           # partials with no visible key (LSE -inf), placed at random
+    seed: int
+
+
+# Backward of the merge of the split-KV prefill's partials at the bottom-right
+# offset shape (B=1, Hq=32, q_len=1024: 32768 rows, 4 key ranges, D=128).
+SPLITK_MERGE_BACKWARD = MergeBwdSpec("splitk_merge_backward", 32768, 4, 128, 256, 20272)
+
+
+def make_bias(shape, dtype="bf16", seed=0, mult=2.0):
+    """An additive bias of `shape`, N(0, 1) * mult rounded to dtype."""
+    g = torch.Generator().manual_seed(seed)
+    return _randn(shape, g, _DTYPES[dtype], mult)
+
+
+def make_prefill_bias_spec(spec: PrefillSpec):
+    """q, k, v of the prefill shape and a per-head bias [1, Hq, q_len, kv_len]."""
+    q, k, v = make_prefill_spec(spec)
+    return q, k, v, make_bias((1, spec.Hq, spec.q_len, spec.kv_len), spec.dtype, spec.seed + 1)
+
+
+def make_decode_bias_spec(spec: DecodeSpec):
+    """Paged decode inputs (make_decode_spec) and a bias [B, Hq, q_len, max_kv_len]."""
+    inp = make_decode_spec(spec)
+    return inp, make_bias((spec.B, spec.Hq, spec.q_len, inp.max_kv_len), spec.dtype, spec.seed + 1)
+
+
+def make_merge_backward_spec(spec: MergeBwdSpec):
+    """Partials of a split-K merge and the gradients of a scalar with respect to
+    its outputs, fp32: o_parts [rows, S, D] ~ N(0, 1), lse_parts [rows, S] ~
+    3 N(0, 1) with `empty` partials set to (0, -inf) and row 0 empty in every
+    range, d_o [rows, D] and d_lse [rows] ~ N(0, 1).  The merged (o, lse) the
+    backward also takes are the merge of these partials."""
+    g = torch.Generator().manual_seed(spec.seed)
+    op = torch.randn((spec.rows, spec.n_splits, spec.D), generator=g)
+    lp = 3.0 * torch.randn((spec.rows, spec.n_splits), generator=g)
+    r = torch.randint(0, spec.rows, (spec.empty,), generator=g)
+    s = torch.randint(0, spec.n_splits, (spec.empty,), generator=g)
+    op[r, s] = 0.0
+    lp[r, s] = float("-inf")
+    op[0] = 0.0
+    lp[0] = float("-inf")
+    d_o = torch.randn((spec.rows, spec.D), generator=g)
+    d_lse = torch.randn((spec.rows,), generator=g)
+    return op, lp, d_o, d_lse
