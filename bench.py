@@ -46,9 +46,9 @@ METRIC = "attention fwd TFLOP/s + % bf16 MFMA peak; decode GB/s + % HBM peak"
 # other source reports traffic null.
 TRAFFIC_MEASUREMENT = {
     "source": "gqa_attention_forward_attn_amd/csrc/prefill_pp.hip",
-    "sha1": "9ba494846a29ff65bfdebb91d2477b01ce562182",
-    "fetch_kib": 24791.2, "write_kib": 33280.0,
-    "copy_fetch_kib": 262156.3, "copy_write_kib": 524288.0,
+    "sha1": "84c254360a1231c141735ae2cb84efa0c4822696",
+    "fetch_kib": 24787.1, "write_kib": 33280.0,
+    "copy_fetch_kib": 262155.5, "copy_write_kib": 524288.0,
 }
 
 
