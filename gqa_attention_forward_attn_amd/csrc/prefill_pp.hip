@@ -248,13 +248,26 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
     const size_t o_row_bytes = PAGED ? (size_t)a.Hq * ROWB : (size_t)ROWB;
 
     // ---- Q (B operand of S^T = K Q^T) ---------------------------------------
+    // Each wave's 32 rows reach LDS by direct loads, whole rows per
+    // instruction, in the layout of a K tile (chunk c of row r at position
+    // c ^ swz(r)) inside ring stages 2 and 3, which no tile occupies before the
+    // first barrier; the operands are read back from there before it.  (Loading
+    // the operands straight into registers touches each 128-byte line of Q
+    // from four instructions, 32 lines per instruction.)
     vec8 qf[DS];
-    {
-        const uint16_t* qp = static_cast<const uint16_t*>(a.q) + row_elt(min(max(my_q, 0), q_len - 1));
+    const int q_stage_off = 2 * STAGEB + wave * (32 * ROWB);
+    auto issue_q = [&]() {
+        const uint16_t* qb = static_cast<const uint16_t*>(a.q);
+        const uint32_t dst = (uint32_t)(uintptr_t)(smem + q_stage_off);
 #pragma unroll
-        for (int ds = 0; ds < DS; ++ds) qf[ds] = __builtin_bit_cast(vec8, ld_global_16(qp + ds * 16 + half * 8));
-    }
-    wait_vmcnt<0>();
+        for (int j = 0; j < CPR / 2; ++j) {
+            const int p = j * 64 + lane;
+            const int r = p / CPR;
+            const int c = (p % CPR) ^ swz<D>(r);
+            const int row = min(max(pos0 + r, 0), q_len - 1);
+            dma16(qb + row_elt(row) + c * 8, __builtin_amdgcn_readfirstlane(dst + j * 1024));
+        }
+    };
 
     // ---- direct global -> LDS tile loads --------------------------------------
     // dense: the (b, g) plane; PAGED: head g inside the pool's token rows
@@ -481,11 +494,23 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
     // A wave's own steps: scores of tile 0, then (softmax of tile t, MFMAs of
     // tile t+1: scores of t+1 and P.V of t) for each t, the last P.V alone.
     // Tile t must be in LDS (this wave's loads done, then the barrier) from
-    // phase 2t on; tile t+2 is issued right after the barrier of phase 2t.
-    // PAGED: the page ids of tile t + 4 are loaded right after tile t + 2, so at
-    // phase 2t the loads younger than those of tile t + 2's pages are tile t+1's
-    // and the pages of t + 3.
+    // phase 2t on.  Issuing a tile's loads slows the issuing wave for a few
+    // hundred cycles, so dense tiles are issued where a wave has slack before
+    // a barrier: at the end of its own softmax phase.  Group 0 issues its part
+    // of tile t+2 after its softmax of tile t (between barriers 2t+1 and
+    // 2t+2), group 1 its part of tile t+3 after its softmax of tile t
+    // (between barriers 2t+2 and 2t+3; tile 2 in its idle first phase).  Stage
+    // j % NST then held tile j-4, whose last reader (group 1's P.V, in the
+    // phase after barrier 2j-5) is done.  At barrier 2t each wave's only loads
+    // younger than tile t's are tile t+1's.
+    // (D = 64 tiles take half the loads and measure better issued right after
+    // the barrier.)  PAGED and D = 64: tile t+2 is issued by every wave right
+    // after the barrier of phase 2t, and the page ids of tile t + 4 right after
+    // it, so at phase 2t the loads younger than those of tile t + 2's pages are
+    // tile t+1's and the pages of t + 3.
+    constexpr bool kLateIssue = !PAGED && D == 128;
     if (n_tiles > 0) {
+        issue_q();
         if constexpr (PAGED) {
             issue_pages(0);
             if (n_tiles > 1) issue_pages(1);
@@ -496,6 +521,20 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
         if (n_tiles > 2) issue_pages(2);
         if (n_tiles > 1) issue_tile(1);
         if (n_tiles > 3) issue_pages(3);
+        // Q (and tile 0) in LDS: read the operands, and finish reading them
+        // before the first barrier, after which tile 2 goes to stage 2
+        if constexpr (!PAGED) {
+            if (n_tiles > 1) wait_vmcnt<2 * LPW>();
+            else wait_vmcnt<0>();
+        }
+        __asm__ __volatile__("" ::: "memory");  // the direct loads wrote LDS
+        {
+            const lds_char* sq = smem + q_stage_off;
+#pragma unroll
+            for (int ds = 0; ds < DS; ++ds)
+                qf[ds] = *reinterpret_cast<const __attribute__((address_space(3))) vec8*>(sq + k_off[ds]);
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        }
         int p = 0;
         auto sync = [&]() {
             if ((p & 1) == 0) {
@@ -507,18 +546,24 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
                 }
             }
             barrier_no_fence();
-            if ((p & 1) == 0 && (p >> 1) + 2 < n_tiles) {
-                issue_tile((p >> 1) + 2);
-                if ((p >> 1) + 4 < n_tiles) issue_pages((p >> 1) + 4);
+            if constexpr (!kLateIssue) {
+                if ((p & 1) == 0 && (p >> 1) + 2 < n_tiles) {
+                    issue_tile((p >> 1) + 2);
+                    if ((p >> 1) + 4 < n_tiles) issue_pages((p >> 1) + 4);
+                }
             }
             ++p;
         };
-        if (grp) sync();  // group 1 starts one phase later
+        if (grp) {  // group 1 starts one phase later
+            sync();
+            if (kLateIssue && n_tiles > 2) issue_tile(2);
+        }
         sync();
         scores_only(0);
         for (int t = 0; t + 1 < n_tiles; ++t) {
             sync();
             valu_phase(t);
+            if (kLateIssue && t + 2 + grp < n_tiles) issue_tile(t + 2 + grp);
             sync();
             mfma_phase(t + 1);
         }
