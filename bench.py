@@ -46,8 +46,8 @@ METRIC = "attention fwd TFLOP/s + % bf16 MFMA peak; decode GB/s + % HBM peak"
 # other source reports traffic null.
 TRAFFIC_MEASUREMENT = {
     "source": "gqa_attention_forward_attn_amd/csrc/prefill_pp.hip",
-    "sha1": "84c254360a1231c141735ae2cb84efa0c4822696",
-    "fetch_kib": 24787.1, "write_kib": 33280.0,
+    "sha1": "5c0e0d22cbb928c9faa5a7f8eb01db85e09aaef8",
+    "fetch_kib": 24759.0, "write_kib": 33280.0,
     "copy_fetch_kib": 262155.5, "copy_write_kib": 524288.0,
 }
 
