@@ -208,7 +208,7 @@ def bench_prefill_bias(spec, steps, warmup):
         "workload": spec.name, "dtype": spec.dtype, "causal": spec.causal,
         "shape": {"B": spec.B, "Hq": spec.Hq, "Hkv": spec.Hkv, "q_len": spec.q_len,
                   "kv_len": spec.kv_len, "D": spec.D, "bias": [1, spec.Hq, spec.q_len, spec.kv_len]},
-        "kernel": "prefill_fwd_mfma<bf16, D=128, causal, bias>",
+        "kernel": "prefill_fwd_pp<bf16, D=128, causal, NH=4, bias>",
         "flop_per_launch": flops,
         "bias_bytes": bias.numel() * bias.element_size(),
         "ms_per_step": wall / steps * 1e3,

@@ -40,7 +40,7 @@ struct PrefillArgs {
     const int* kv_indices;        // page ids
     const int* kv_last_page_len;  // [B] tokens in each last page, or nullptr (full pages)
     int page_shift;               // log2(page_size)
-    // Additive bias (four-wave kernel, dense only): bias(b, h, i, j) =
+    // Additive bias (dense only): bias(b, h, i, j) =
     // bias[b * bias_sb + h * bias_sh + i * bias_sq + j] in the input dtype,
     // added to the scores in the softmax's natural units; bias_k = 1 / scale.
     const uint16_t* bias;
@@ -55,6 +55,9 @@ enum class PrefillKernel { kAuto, kPingPong, kFourWave };
 hipError_t launch_prefill(PrefillArgs a, int D, bool causal, int dtype, PrefillKernel kernel, hipStream_t stream);
 // The same with the additive bias of a.bias (bf16 / fp16, four-wave kernel).
 hipError_t launch_prefill_bias(PrefillArgs a, int D, bool causal, int dtype, hipStream_t stream);
+// The same on the ping-pong kernel: D = 128, kv_len a multiple of 64, bias
+// base and row strides 16-byte aligned (callers check).
+hipError_t launch_prefill_pp_bias(PrefillArgs a, bool causal, int dtype, hipStream_t stream);
 // Ragged batch of requests over a paged K/V cache (bf16 / fp16): the ping-pong
 // kernel for batches that give every CU a workgroup, else the four-wave kernel
 // (or the one `kernel` forces).

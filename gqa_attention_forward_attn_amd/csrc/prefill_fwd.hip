@@ -655,6 +655,10 @@ hipError_t launch_prefill(PrefillArgs a, int D, bool causal, int dtype, PrefillK
 }
 
 hipError_t launch_prefill_bias(PrefillArgs a, int D, bool causal, int dtype, hipStream_t stream) {
+    // the ping-pong kernel takes whole 64-key tiles of 16-byte aligned bias rows
+    if (D == 128 && a.kv_len % 64 == 0 && (reinterpret_cast<uintptr_t>(a.bias) & 15) == 0 && a.bias_sb % 8 == 0 &&
+        a.bias_sh % 8 == 0 && a.bias_sq % 8 == 0)
+        return launch_prefill_pp_bias(a, causal, dtype, stream);
     // four keys per load when every bias row starts 8-byte aligned
     const bool vec = (reinterpret_cast<uintptr_t>(a.bias) & 7) == 0 && a.bias_sb % 4 == 0 && a.bias_sh % 4 == 0 &&
                      a.bias_sq % 4 == 0;

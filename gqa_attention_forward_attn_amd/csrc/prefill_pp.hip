@@ -117,7 +117,19 @@ __device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
 // [total_q, Hq].  The page id of every key row of a tile is brought into a
 // per-wave LDS ring by a direct load two tiles before the tile itself, so the
 // tile loads read their page ids from LDS.
-template <class TAG, int D, bool CAUSAL, int NH, bool PAGED>
+// 16-bit additive bias element -> fp32
+__device__ __forceinline__ float bias_f32(bf16_tag, uint32_t u16) { return __builtin_bit_cast(float, u16 << 16); }
+__device__ __forceinline__ float bias_f32(f16_tag, uint32_t u16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)u16);
+}
+
+// BIAS (dense keys, D = 128, whole 64-key tiles, 16-byte aligned bias rows):
+// the additive bias of splitk_kernels.py (`_fwd_kernel_splitK`,
+// HAS_ADDITIVE_BIAS).  Each wave brings the bias of its 32 rows for the next
+// tile into its own 4 KB LDS buffer by direct loads at the end of its softmax
+// phase, next to its part of the K/V tiles, and adds it to the scores at the
+// start of the following softmax phase.
+template <class TAG, int D, bool CAUSAL, int NH, bool PAGED, bool BIAS = false>
 __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
     constexpr int NW = 8;                  // waves per workgroup
     constexpr int BN = 64;                 // keys per tile
@@ -137,7 +149,15 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem_raw[NST * STAGEB];
     lds_char* smem = (lds_char*)smem_raw;
     // PAGED: page ids of the rows of tiles t .. t + 3, ring slot t % NST, per wave
-    __shared__ __attribute__((aligned(16))) int pg_ring[PAGED ? NW * NST * BN : 1];
+    // BIAS: one 4 KB buffer per wave (32 rows x 64 keys); PAGED and BIAS never
+    // meet, so the page ring and the bias buffers share one array (the bias
+    // kernel's LDS is then 160 KB in all)
+    constexpr int BWB = 32 * BN * 2;       // BIAS: bytes of one wave's bias buffer
+    constexpr int BW = BWB / 1024;         // BIAS: direct loads per wave per tile
+    static_assert(!BIAS || (!PAGED && D == 128), "bias: dense keys, D = 128");
+    __shared__ __attribute__((aligned(16))) char aux_raw[PAGED ? NW * NST * BN * 4 : (BIAS ? NW * BWB : 16)];
+    int* pg_ring = reinterpret_cast<int*>(aux_raw);
+    [[maybe_unused]] char* bias_raw = aux_raw;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -328,6 +348,23 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
         }
     };
 
+    // BIAS: rows pos0 .. pos0 + 31 of the bias for the keys of tile t; 16-byte
+    // chunk c of row r at chunk position c ^ (r & 7) of a 128-byte LDS row
+    [[maybe_unused]] auto issue_bias = [&](int t) {
+        if constexpr (BIAS) {
+            const int k0 = (t_lo + t) * BN;
+            const uint16_t* bh = a.bias + (long long)b * a.bias_sb + (long long)h * a.bias_sh + k0;
+            const uint32_t dst = (uint32_t)(uintptr_t)((lds_char*)bias_raw + wave * BWB);
+#pragma unroll
+            for (int j = 0; j < BW; ++j) {
+                const int p = j * 64 + lane;
+                const int r = p >> 3, c = (p & 7) ^ (r & 7);
+                const int row = min(max(pos0 + r, 0), q_len - 1);
+                dma16(bh + (long long)row * a.bias_sq + c * 8, __builtin_amdgcn_readfirstlane(dst + j * 1024));
+            }
+        }
+    };
+
     // ---- per-lane LDS read offsets ---------------------------------------------
     int k_off[DS];  // K operand: row l32 (+32 kh), chunk 2 ds + half
     {
@@ -443,6 +480,28 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
 
     // VALU phase of tile t: mask, row max, lazy rescale, weights
     auto valu_phase = [&](int t) {
+        if constexpr (BIAS) {
+            // this wave's bias of tile t: its loads were followed only by its
+            // part of tile t + 1 + grp (tile 0's bias is waited for with Q)
+            if (t > 0) {
+                if (t + 1 + grp < n_tiles) wait_vmcnt<2 * LPW>();
+                else wait_vmcnt<0>();
+                __asm__ __volatile__("" ::: "memory");
+            }
+            const lds_char* bb = (const lds_char*)bias_raw + wave * BWB + l32 * (BN * 2) + half * 8;
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const u32x2 w = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(
+                        bb + (((kh * 4 + r4) ^ (l32 & 7)) * 16));
+                    // keys 32 kh + 8 r4 + 4 half + 0..3: s * c gains log2(e) * bias (bias_k = 1 / scale)
+                    s[kh][4 * r4] = fmaf(bias_f32(TAG(), w[0] & 0xffffu), a.bias_k, s[kh][4 * r4]);
+                    s[kh][4 * r4 + 1] = fmaf(bias_f32(TAG(), w[0] >> 16), a.bias_k, s[kh][4 * r4 + 1]);
+                    s[kh][4 * r4 + 2] = fmaf(bias_f32(TAG(), w[1] & 0xffffu), a.bias_k, s[kh][4 * r4 + 2]);
+                    s[kh][4 * r4 + 3] = fmaf(bias_f32(TAG(), w[1] >> 16), a.bias_k, s[kh][4 * r4 + 3]);
+                }
+        }
         if (t >= n_full) {  // diagonal / tail tile
             const int k0 = (t_lo + t) * BN;
 #pragma unroll
@@ -511,6 +570,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
     constexpr bool kLateIssue = !PAGED && D == 128;
     if (n_tiles > 0) {
         issue_q();
+        issue_bias(0);
         if constexpr (PAGED) {
             issue_pages(0);
             if (n_tiles > 1) issue_pages(1);
@@ -541,7 +601,15 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
                 const int t = p >> 1;
                 if (t < n_tiles) {
                     if (PAGED && t + 3 < n_tiles) wait_vmcnt<2 * LPW + 1>();   // tile t, pages of t + 2
-                    else if (t + 1 < n_tiles) wait_vmcnt<2 * LPW>();           // tile t (pages of t + 2 if any)
+                    else if (BIAS) {
+                        // after tile t this wave issued the bias of tile t (group 0 from
+                        // t = 1 on, group 1 from t = 2 on) and its part of tile t + 1
+                        const bool b_after = t > 1 || (t == 1 && grp == 0);
+                        if (b_after && t + 1 < n_tiles) wait_vmcnt<BW + 2 * LPW>();
+                        else if (b_after) wait_vmcnt<BW>();
+                        else if (t + 1 < n_tiles) wait_vmcnt<2 * LPW>();
+                        else wait_vmcnt<0>();
+                    } else if (t + 1 < n_tiles) wait_vmcnt<2 * LPW>();          // tile t (pages of t + 2 if any)
                     else wait_vmcnt<0>();
                 }
             }
@@ -563,6 +631,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_pp(PrefillArgs a) {
         for (int t = 0; t + 1 < n_tiles; ++t) {
             sync();
             valu_phase(t);
+            if (BIAS) issue_bias(t + 1);  // before the tile: the next softmax phase waits for it alone
             if (kLateIssue && t + 2 + grp < n_tiles) issue_tile(t + 2 + grp);
             sync();
             mfma_phase(t + 1);
@@ -672,7 +741,7 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a, long 
     if (d0 == 0) a.lse[row] = W > 0.f ? M + fast_log2(W) * kLn2 : -INFINITY;
 }
 
-template <class TAG, int D, bool CAUSAL, int NH, bool PAGED>
+template <class TAG, int D, bool CAUSAL, int NH, bool PAGED, bool BIAS = false>
 hipError_t launch_pp(PrefillArgs a, hipStream_t stream) {
     constexpr int POS = 256 / NH;
     a.n_pos_tiles = (a.q_len + POS - 1) / POS;
@@ -685,7 +754,7 @@ hipError_t launch_pp(PrefillArgs a, hipStream_t stream) {
     // from HBM again, and the XCD-aware order keeps them resident instead.
     const long long kv_bytes_head = (long long)a.kv_len * D * 4;  // 16-bit K and V of one (b, kv head)
     a.xcd_order = !PAGED && a.kv_splits <= 1 && a.n_rest >= 8 && (a.n_rest + 7) / 8 * kv_bytes_head > (2LL << 20);
-    hipLaunchKernelGGL((prefill_fwd_pp<TAG, D, CAUSAL, NH, PAGED>), dim3((unsigned)blocks), dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((prefill_fwd_pp<TAG, D, CAUSAL, NH, PAGED, BIAS>), dim3((unsigned)blocks), dim3(512), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.kv_splits <= 1) return e;
     const long long rows = (long long)a.B * a.Hq * a.q_len;
@@ -726,6 +795,20 @@ hipError_t launch_prefill_split(PrefillArgs a, int D, bool causal, int dtype, hi
 hipError_t launch_prefill_pp(PrefillArgs a, int D, bool causal, int dtype, hipStream_t stream) {
     if (dtype == kDtypeBF16) return dispatch_d<bf16_tag, false>(a, D, causal, stream);
     return dispatch_d<f16_tag, false>(a, D, causal, stream);
+}
+
+template <class TAG, bool CAUSAL>
+hipError_t dispatch_nh_bias(PrefillArgs a, hipStream_t stream) {
+    if (a.group % 8 == 0) return launch_pp<TAG, 128, CAUSAL, 8, false, true>(a, stream);
+    if (a.group % 4 == 0) return launch_pp<TAG, 128, CAUSAL, 4, false, true>(a, stream);
+    if (a.group % 2 == 0) return launch_pp<TAG, 128, CAUSAL, 2, false, true>(a, stream);
+    return launch_pp<TAG, 128, CAUSAL, 1, false, true>(a, stream);
+}
+
+hipError_t launch_prefill_pp_bias(PrefillArgs a, bool causal, int dtype, hipStream_t stream) {
+    a.kv_splits = 1;
+    if (dtype == kDtypeBF16) return causal ? dispatch_nh_bias<bf16_tag, true>(a, stream) : dispatch_nh_bias<bf16_tag, false>(a, stream);
+    return causal ? dispatch_nh_bias<f16_tag, true>(a, stream) : dispatch_nh_bias<f16_tag, false>(a, stream);
 }
 
 hipError_t launch_prefill_pp_paged(PrefillArgs a, int D, bool causal, int dtype, hipStream_t stream) {

@@ -134,11 +134,15 @@ gqa_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, floa
  * are all masked gets o = 0, lse = -inf.  +inf or NaN biases are undefined.
  *
  *   bias  device memory, read only at (b, h, i, j) with j < kv_len; 2-byte
- *         aligned (rows that start 8-byte aligned, i.e. all strides multiples
- *         of 4 and bias 8-byte aligned, are read four keys at a time).
+ *         aligned.  With D = 128, kv_len a multiple of 64, bias 16-byte
+ *         aligned and all strides multiples of 8, the ping-pong kernel runs
+ *         (the bias of a 64-key tile reaches LDS by direct loads beside the
+ *         K/V tile); otherwise the four-wave kernel (rows that start 8-byte
+ *         aligned, i.e. all strides multiples of 4 and bias 8-byte aligned,
+ *         are read four keys at a time).
  *
  * Other arguments, layouts and results as attn_fwd; dtype F32 returns
- * GQA_ERR_UNSUPPORTED.  Runs the four-wave kernel.
+ * GQA_ERR_UNSUPPORTED.
  */
 gqa_status_t attn_fwd_bias(const void* q, const void* k, const void* v, const void* bias, long long bias_stride_b,
                            long long bias_stride_h, long long bias_stride_q, void* o, float* lse, int B, int Hq,

@@ -55,6 +55,12 @@ PREFILL_BIAS = [
     (1, 32, 4, 96, 416, 128, "bf16", True, "keys_only", 0),    # G = 8 with offset, one row for all
     (1, 6, 3, 257, 257, 128, "f16", True, "full", 1),          # rows unaligned (a view one key in)
     (3, 4, 4, 65, 1, 64, "bf16", False, "full", 0),            # one key
+    # D = 128, whole 64-key tiles, 16-byte aligned rows: the ping-pong kernel
+    (2, 32, 8, 512, 512, 128, "bf16", True, "per_head", 0),
+    (1, 8, 2, 200, 384, 128, "f16", False, "per_batch", 0),
+    (1, 16, 4, 256, 1024, 128, "bf16", True, "keys_only", 0),  # offset 768, one row for all
+    (2, 4, 4, 64, 128, 128, "bf16", True, "full", 0),          # G = 1
+    (1, 16, 2, 100, 64, 128, "f16", True, "full", 0),          # q_len > kv_len: one tile, empty rows
 ]
 
 
@@ -79,6 +85,17 @@ def test_prefill_zero_bias_is_the_plain_kernel_bitwise():
     zero = torch.zeros(1, 1, 1, 300, dtype=torch.bfloat16, device="cuda")
     for causal in (True, False):
         o1, l1 = gqa.attn_fwd(qd, kd, vd, causal=causal, scale=0.09, kernel="fourwave")
+        o2, l2 = gqa.attn_fwd_bias(qd, kd, vd, zero, causal=causal, scale=0.09)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_prefill_zero_bias_is_the_pingpong_kernel_bitwise():
+    # a shape the ping-pong kernel takes with a bias (D = 128, whole tiles)
+    q, k, v = W.make_prefill(2, 8, 2, 300, 256, 128, "bf16", seed=3)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    zero = torch.zeros(1, 1, 1, 256, dtype=torch.bfloat16, device="cuda")
+    for causal in (True, False):
+        o1, l1 = gqa.attn_fwd(qd, kd, vd, causal=causal, scale=0.09, kernel="pingpong")
         o2, l2 = gqa.attn_fwd_bias(qd, kd, vd, zero, causal=causal, scale=0.09)
         assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
