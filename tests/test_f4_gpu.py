@@ -209,11 +209,27 @@ def _merge_inputs(rows, S, D, seed, n_empty):
     return op, lp, o, lse, d_o, d_lse
 
 
-@pytest.mark.parametrize("rows,S,D", [(2048, 16, 128), (300, 1, 64), (77, 5, 96), (512, 64, 128), (9, 3, 512)])
-def test_merge_backward_matches_oracle(rows, S, D):
-    print(f"merge backward rows={rows} S={S} D={D}", flush=True)
+def _on_gpu(x, misalign):
+    """x on the GPU; misalign: a contiguous view starting 4 bytes into its
+    allocation, so rows are not 16-byte aligned (the one-float-per-lane path)."""
+    if not misalign:
+        return torch.from_numpy(x).cuda()
+    flat = torch.empty(x.size + 1, dtype=torch.float32, device="cuda")
+    view = flat[1:].view(x.shape)
+    view.copy_(torch.from_numpy(x))
+    return view
+
+
+# (rows, S, D, misalign): D a multiple of 4 and aligned rows take the 16-byte
+# kernel (lane groups of 16, 32 or 64; D = 512 two pieces per lane); D = 66 and
+# the misaligned case the one-float-per-lane kernel
+@pytest.mark.parametrize("rows,S,D,misalign", [(2048, 16, 128, False), (300, 1, 64, False), (77, 5, 96, False),
+                                               (512, 64, 128, False), (9, 3, 512, False), (130, 3, 66, False),
+                                               (257, 4, 128, True), (33, 7, 256, False), (65, 2, 20, False)])
+def test_merge_backward_matches_oracle(rows, S, D, misalign):
+    print(f"merge backward rows={rows} S={S} D={D} misalign={misalign}", flush=True)
     op, lp, o, lse, d_o, d_lse = _merge_inputs(rows, S, D, seed=rows + S + D, n_empty=rows // 3)
-    dev = [torch.from_numpy(x).cuda() for x in (op, lp, o, lse, d_o, d_lse)]
+    dev = [_on_gpu(x, misalign) for x in (op, lp, o, lse, d_o, d_lse)]
     dop, dlp = gqa.attn_splitk_merge_backward(*dev)
     torch.cuda.synchronize()
     dop, dlp = dop.double().cpu().numpy(), dlp.double().cpu().numpy()
