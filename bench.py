@@ -291,7 +291,7 @@ def bench_merge_backward(spec, steps, warmup):
     return {
         "workload": spec.name, "dtype": "f32",
         "shape": {"rows": spec.rows, "n_splits": spec.n_splits, "D": spec.D},
-        "kernel": "merge_backward_kernel (one wave per row)",
+        "kernel": "merge_backward_vec_kernel<32, 1, 2> (one wave per row, two partials at a time, 16-byte accesses)",
         "bytes_per_step": nbytes,
         "ms_per_step": wall / steps * 1e3,
         "kernel_ms_mean": kern_s * 1e3, "call_span_ms_min": float(per.min()) * 1e3,
