@@ -715,23 +715,47 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a, long 
     const int d0 = (int)(i - row * G) * 8;
     const int S = a.kv_splits;
     const float* pl = a.part_lse + row * S;
-    float M = -INFINITY;
-    for (int sp = 0; sp < S; ++sp) M = fmaxf(M, pl[sp]);
-    float W = 0.f, O[8];
+    // ranges in groups of 8: every LSE and partial output of a group is loaded
+    // before any is used (an empty range holds (0, -inf): weight 0 on a zero
+    // row), with a running maximum across groups
+    float M = -INFINITY, W = 0.f, O[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) O[e] = 0.f;
-    for (int sp = 0; sp < S; ++sp) {
-        const float lv = pl[sp];
-        if (lv == -INFINITY) continue;
-        const float w = fast_exp2((lv - M) * kLog2e);
-        W += w;
-        const float* po = a.part_o + (row * S + sp) * D + d0;
-        const f32x4 x0 = *reinterpret_cast<const f32x4*>(po);
-        const f32x4 x1 = *reinterpret_cast<const f32x4*>(po + 4);
+    for (int s0 = 0; s0 < S; s0 += 8) {
+        float lv[8];
+        f32x4 x0[8], x1[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            O[e] += w * x0[e];
-            O[4 + e] += w * x1[e];
+        for (int k = 0; k < 8; ++k) {
+            if (s0 + k < S) {
+                const float* po = a.part_o + (row * S + s0 + k) * D + d0;
+                lv[k] = pl[s0 + k];
+                x0[k] = *reinterpret_cast<const f32x4*>(po);
+                x1[k] = *reinterpret_cast<const f32x4*>(po + 4);
+            }
+        }
+        float mg = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (s0 + k < S) mg = fmaxf(mg, lv[k]);
+        const float Mn = fmaxf(M, mg);
+        if (Mn > M && M != -INFINITY) {  // a later group raised the maximum
+            const float r = fast_exp2((M - Mn) * kLog2e);
+            W *= r;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) O[e] *= r;
+        }
+        M = Mn;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            if (s0 + k < S) {
+                const float w = lv[k] == -INFINITY ? 0.f : fast_exp2((lv[k] - M) * kLog2e);
+                W += w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    O[e] += w * x0[k][e];
+                    O[4 + e] += w * x1[k][e];
+                }
+            }
         }
     }
     const float inv = W > 0.f ? 1.f / W : 0.f;

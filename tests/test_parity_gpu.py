@@ -98,6 +98,8 @@ SPLIT = [
     (2, 4, 2, 300, 100, 64, "bf16", True, 3),       # q_len > kv_len: leading rows see no key
     (1, 6, 3, 257, 257, 128, "f16", True, 8),       # more ranges than some row blocks have tiles
     (1, 12, 4, 64, 64, 64, "bf16", True, 2),        # G = 3, a single key tile
+    (1, 8, 2, 200, 1500, 128, "bf16", True, 13),    # more than 8 ranges: the merge takes them in groups
+    (1, 4, 4, 64, 2048, 64, "f16", False, 20),      # 16 non-empty ranges, then 4 empty ones
 ]
 
 
