@@ -434,6 +434,8 @@ gqa_status_t attn_decode_splitk_noalloc(const void* q, const void* k, const void
  *
  * All device pointers, 4-byte aligned, owned by the caller; outputs must not
  * alias inputs.  1 <= n_splits <= 65536, 1 <= D <= 512, 0 <= rows < 2^36.
+ * With D a multiple of 4 and o_parts, o, d_o, d_o_parts 16-byte aligned the
+ * rows move in 16-byte pieces (faster); any other case one float per lane.
  * rows == 0 returns GQA_OK without launching.  Arithmetic in fp32.
  * Returns GQA_ERR_INVALID_ARG / GQA_ERR_HIP or GQA_OK.
  */
