@@ -46,8 +46,8 @@ METRIC = "attention fwd TFLOP/s + % bf16 MFMA peak; decode GB/s + % HBM peak"
 # other source reports traffic null.
 TRAFFIC_MEASUREMENT = {
     "source": "gqa_attention_forward_attn_amd/csrc/prefill_pp.hip",
-    "sha1": "a93ad5a5784f7691aa52476c4ec63c1ab14a69f4",
-    "fetch_kib": 24763.4, "write_kib": 33280.0,
+    "sha1": "148b57d01e21ee7c10f1392df0cb649002db4a05",
+    "fetch_kib": 24780.1, "write_kib": 33280.0,
     "copy_fetch_kib": 262155.5, "copy_write_kib": 524288.0,
 }
 
