@@ -31,10 +31,12 @@
 //                                         transposed (ds_read_b64_tr_b16)
 //
 // The S^T result layout (lane: head l%16, tokens 4(l/16)..+3) is exactly the
-// A-operand layout of the P.V MFMA, so P never leaves its registers.  Loads run
-// NST-1 slices ahead of the arithmetic and no barrier is taken in the loop:
-// every wave waits only for its own loads.  The NW per-wave partial results are
-// merged through LDS at the end of the chunk.
+// A-operand layout of the P.V MFMA, so P never leaves its registers.  Each wave
+// keeps one slice in flight: slice k + 1 leaves once slice k has landed and
+// loads while slice k is computed (more loads in flight per CU measured slower,
+// the memory system queueing them rather than streaming faster).  No barrier is
+// taken in the loop: every wave waits only for its own loads.  The NW per-wave
+// partial results are merged through LDS at the end of the chunk.
 #include "gqa_device.hpp"
 #include "gqa_kernels.hpp"
 
@@ -53,6 +55,11 @@ constexpr float kRescaleLog2 = 8.f;
 // K/V addressing of the split kernel
 enum { kDense = 0, kPaged = 1, kPagedSmall = 2 };
 
+// waves and ring stages of the 16-bit split kernel.  A wave has one slice in
+// flight and one being read, so two stages would do; four make the workgroup's
+// LDS (q rows + 4 rings, 132 KB at D = 128) hold it to one workgroup per CU,
+// i.e. four slices in flight per CU: two workgroups per CU (two stages, eight
+// waves) measured 7-9 % slower on the decode workloads.
 #ifndef DEC_NW
 #define DEC_NW 4
 #endif
@@ -190,16 +197,17 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
     constexpr int SLB = kSlice * ROWB;      // bytes of a K (or V) slice
     constexpr int BSB = BIAS ? 16 * kSlice * 2 : 0;  // bias of a slice: 16 columns x 16 keys
     constexpr int STB = 2 * SLB + BSB;      // stage: K slice, V slice[, bias]
-    constexpr int QB = 16 * ROWB;           // q rows of the head block
-    constexpr int WAVEB = QB + NST * STB;   // LDS per wave
+    constexpr int QB = 16 * ROWB;           // q rows of the head block, shared by the waves
+    constexpr int RINGB = NST * STB;        // LDS ring of a wave
     constexpr int KS = D / 32;              // k-steps of S^T = K q^T
     constexpr int NB = D / 16;              // 16-column blocks of O
     constexpr int PER_SLICE = 2 * NI + (BIAS ? 2 : 0);
     static_assert((NST - 1) * PER_SLICE < 64, "vmcnt range");
     static_assert((NST & (NST - 1)) == 0, "NST must be a power of two");
-    static_assert((NW * 16 * (D + 4) + 3 * NW * 16) * 4 <= NW * WAVEB, "merge buffers must fit in the ring");
+    static_assert(NST >= 2, "the slice being read and the slice in flight");
+    static_assert((NW * 16 * (D + 4) + 3 * NW * 16) * 4 <= QB + NW * RINGB, "merge buffers must fit in LDS");
 
-    __shared__ __attribute__((aligned(1024))) char smem_raw[NW * WAVEB];
+    __shared__ __attribute__((aligned(1024))) char smem_raw[QB + NW * RINGB];
     lds_char* smem = (lds_char*)smem_raw;
 
     const int tid = threadIdx.x;
@@ -231,8 +239,9 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
     const int n_sl = span > kSlice * wave ? (span - kSlice * wave + stride - 1) / stride : 0;
     const int T0 = lo + kSlice * wave;
 
-    const lds_char* wlds = smem + wave * WAVEB;
+    const lds_char* wlds = smem + QB + wave * RINGB;  // this wave's ring
     const uint32_t wlds_u = (uint32_t)(uintptr_t)wlds;
+    const uint32_t q_u = (uint32_t)(uintptr_t)smem;
 
     // per-lane constants of the direct loads: lane -> (row in instruction, physical chunk)
     const int drow = lane / CPR;
@@ -268,19 +277,20 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
             brow[j] = a.bias + (long long)b * a.bias_sb + (long long)h * a.bias_sh + (long long)qi * a.bias_sq;
         }
     }
-    auto issue = [&](int k) {
+    // drain: wait for every load in flight first (after the addresses are
+    // computed, so that the slice's loads leave as soon as the previous ones
+    // have landed)
+    auto issue = [&](int k, bool drain) {
         const int T = T0 + stride * k;
-        const uint32_t st = __builtin_amdgcn_readfirstlane(wlds_u + QB + (k & (NST - 1)) * STB);
+        const uint32_t st = __builtin_amdgcn_readfirstlane(wlds_u + (k & (NST - 1)) * STB);
         const int last = hi - 1 - T;  // rows of the slice at or past `last` repeat row `last`
-        if constexpr (BIAS) {
-            // key pairs past the chunk read the pair of its last key; that pair
-            // may hold one key past the sequence (rows are readable up to an
-            // even key count)
-            const int t = T + min(2 * (lane & 7), last & ~1);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) dma4(brow[j] + t, st + 2 * SLB + j * 256);
-        }
         if (PG == kPagedSmall) {
+            if (drain) wait_vm<0>();
+            if constexpr (BIAS) {
+                const int t = T + min(2 * (lane & 7), last & ~1);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) dma4(brow[j] + t, st + 2 * SLB + j * 256);
+            }
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
                 const int t = T + min(urow[i], last);
@@ -302,11 +312,22 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
         }
         const char* kb = kbytes + row0 * 2;
         const char* vb = vbytes + row0 * 2;
+        uint32_t voff_b[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) voff_b[i] = (uint32_t)(min(urow[i], last) * (int)tok_stride + lcol[i]) * 2u;
+        if (drain) wait_vm<0>();
+        if constexpr (BIAS) {
+            // key pairs past the chunk read the pair of its last key; that pair
+            // may hold one key past the sequence (rows are readable up to an
+            // even key count)
+            const int t = T + min(2 * (lane & 7), last & ~1);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) dma4(brow[j] + t, st + 2 * SLB + j * 256);
+        }
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const uint32_t voff = (uint32_t)(min(urow[i], last) * (int)tok_stride + lcol[i]) * 2u;
-            dma16(kb, voff, st + i * 1024);
-            dma16(vb, voff, st + SLB + i * 1024);
+            dma16(kb, voff_b[i], st + i * 1024);
+            dma16(vb, voff_b[i], st + SLB + i * 1024);
         }
     };
 
@@ -315,19 +336,31 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    if (n_sl > 0) {
-        // q rows of the head block (rows >= nh repeat the last head; their
-        // operand lanes are zeroed below)
+    {
+        // q rows of the head block, one buffer for the workgroup: wave w loads
+        // rows RPI i .. RPI i + RPI - 1 for i = w, w + NW, ... (rows >= nh repeat
+        // the last head; their operand lanes are zeroed below)
         const int nqi = (nh + RPI - 1) / RPI;
-        for (int i = 0; i < nqi; ++i) {
+        for (int i = wave; i < nqi; i += NW) {
             const int r = min(RPI * i + drow, nh - 1);
             const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (qrow0 + r) * D +
                                  (dchk ^ swz<D>(RPI * i + drow)) * 8;
-            dma16(qp, __builtin_amdgcn_readfirstlane(wlds_u + i * 1024));
+            dma16(qp, __builtin_amdgcn_readfirstlane(q_u + i * 1024));
         }
-        const int pro = min(NST - 1, n_sl);
-        for (int k = 0; k < pro; ++k) issue(k);
-        wait_slices<PER_SLICE>(pro);
+    }
+    // the page ids are awaited here, before any slice is issued (the compiler
+    // does not see the direct loads: a wait for them inside the loop would
+    // also wait for every slice in flight)
+    __asm__ __volatile__("" ::"v"(pgv));
+    if (n_sl > 0) {
+        issue(0, false);
+        wait_vm<PER_SLICE>();  // this wave's q rows (loaded before its first slice)
+    } else {
+        wait_vm<0>();
+    }
+    __syncthreads();  // ... and every other wave's
+
+    if (n_sl > 0) {
 
         // q^T as the B operand: lane l holds head l % 16, dims 32 ks + 8 (l / 16)..+7
         const int hrow = lane & 15;
@@ -335,7 +368,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
         u32x4 qop[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const u32x4 x = lds16(wlds + hrow * ROWB + (((4 * ks + kq) ^ swz<D>(hrow)) << 4));
+            const u32x4 x = lds16(smem + hrow * ROWB + (((4 * ks + kq) ^ swz<D>(hrow)) << 4));
             qop[ks] = hrow < nh ? x : u32x4{0u, 0u, 0u, 0u};
         }
         // LDS offsets of the K operand (row l % 16) and of the transposed V reads
@@ -358,10 +391,13 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
         const int lim_lo = min(hi, len - (a.q_len - 1));  // smallest limit of the block
 
         for (int k = 0; k < n_sl; ++k) {
-            if (k + NST - 1 < n_sl) issue(k + NST - 1);
-            wait_slices<PER_SLICE>(min(NST - 1, n_sl - 1 - k));
+            // one slice in flight per wave: slice k + 1 leaves once slice k,
+            // the only load in flight, has landed, and loads while slice k is
+            // computed
+            if (k + 1 < n_sl) issue(k + 1, true);
+            else wait_vm<0>();
 
-            const lds_char* st = wlds + QB + (k & (NST - 1)) * STB;
+            const lds_char* st = wlds + (k & (NST - 1)) * STB;
             f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) sc = mfma16x32(TAG(), lds16(st + koff[ks]), qop[ks], sc);
