@@ -153,6 +153,7 @@ DECODE_BIAS = [
     (4, 8, 2, 64, "f16", 1, 16, (1, 700), 5, "per_head"),
     (3, 32, 4, 128, "bf16", 4, 64, (3, 900), 7, "full"),             # multi-query, some sequences < q_len
     (5, 16, 16, 64, "bf16", 2, 1, (1, 300), 3, "per_batch"),        # G = 1, pages of one token
+    (2, 8, 2, 128, "bf16", 1, 256, (9000, 20000), 1, "per_head"),   # chunks of > 64 slices per wave
 ]
 
 

@@ -285,6 +285,29 @@ def test_decode_cases(case):
     check(o, l, o_ref, l_ref, dt, str(case))
 
 
+# Chunks of more than 4096 keys: a wave's 16-token slices go round-robin over
+# the 4 waves, so past its 64th slice a wave reads each slice's page id from the
+# block table itself instead of from the per-lane list loaded with the chunk.
+LONG_CHUNK = [
+    # B, Hq, Hkv, D, dtype, len_lo, len_hi, page_size, n_splits
+    (2, 8, 2, 128, "bf16", 9000, 20000, 256, 1),
+    (2, 8, 2, 64, "f16", 9000, 20000, 16, 2),
+]
+
+
+@pytest.mark.parametrize("case", LONG_CHUNK, ids=lambda c: "-".join(map(str, c)))
+def test_decode_long_chunks(case):
+    B, Hq, Hkv, D, dt, lo, hi, ps, ns = case
+    print(f"decode long chunks {case}", flush=True)
+    inp = W.make_decode(B, Hq, Hkv, D, dt, seed=sum(case[:4]) + hi, len_lo=lo, len_hi=hi, page_size=ps)
+    assert int(inp.seq_lens.min()) > 4096 * ns  # every chunk spans more than 64 slices per wave
+    scale = W.fp32_scale(D)
+    o, l = gpu_decode(inp, ns, scale)
+    o_ref, l_ref = oracle.attn_decode(inp.q, inp.k_cache, inp.v_cache, inp.seq_lens, scale,
+                                      block_table=inp.block_table, max_kv_len=inp.max_kv_len)
+    check(o, l, o_ref, l_ref, dt, str(case))
+
+
 def test_decode_empty_and_short_sequences():
     inp = W.make_decode(4, 8, 2, 128, "bf16", seed=5, seq_lens=[0, 1, 64, 65], page_size=64, max_pages=2)
     inp.block_table[0, 0] = 0  # never read for an empty sequence
@@ -396,6 +419,16 @@ def test_decode_multi_cases(case):
     o, l = gpu_decode_multi(inp, ns, scale)
     o_ref, l_ref = oracle_multi(inp, scale)
     check(o, l, o_ref, l_ref, dt, str(case))
+
+
+def test_decode_multi_long_chunks():
+    # one chunk of 9000-20000 keys per sequence: page ids past a wave's 64th
+    # slice come from the block table directly
+    print("decode multi long chunks", flush=True)
+    inp = W.make_decode(2, 8, 2, 128, "bf16", seed=77, len_lo=9000, len_hi=20000, page_size=64, q_len=4)
+    o, l = gpu_decode_multi(inp, 1, 0.088)
+    o_ref, l_ref = oracle_multi(inp, 0.088)
+    check(o, l, o_ref, l_ref, "bf16", "multi long chunks")
 
 
 def test_decode_multi_short_sequences_and_invisible_chunks():
@@ -593,6 +626,15 @@ def test_decode_fp8_cases(case):
     o, l = gpu_decode_fp8(inp, ns, scale)
     o_ref, l_ref = oracle_fp8(inp, scale)
     check(o, l, o_ref, l_ref, dt, str(case))
+
+
+def test_decode_fp8_long_chunks():
+    # one chunk of 9000-20000 keys per sequence (more than 64 slices per wave)
+    print("fp8 decode long chunks", flush=True)
+    inp = W.make_decode_fp8(2, 8, 2, 128, "bf16", seed=78, len_lo=9000, len_hi=20000, page_size=256)
+    o, l = gpu_decode_fp8(inp, 1, 0.088)
+    o_ref, l_ref = oracle_fp8(inp, 0.088)
+    check(o, l, o_ref, l_ref, "bf16", "fp8 long chunks")
 
 
 def test_decode_fp8_empty_and_short_sequences():
